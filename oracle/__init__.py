@@ -1,0 +1,21 @@
+"""CPU oracle for exact attention — test infrastructure, not part of the library.
+
+Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py``.  See ``oracle/attention.py`` for the definitions and sources.
+"""
+from .attention import (  # noqa: F401
+    compare,
+    default_scale,
+    kv_head,
+    masked_softmax,
+    merge_partials,
+    online_softmax_stats,
+    ref_bwd,
+    ref_decode,
+    ref_fwd,
+    ref_fwd_rows,
+    ref_probs,
+    scores,
+    tiled_fwd,
+    valid_mask,
+)

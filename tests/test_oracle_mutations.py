@@ -1,0 +1,168 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant patches one internal step of ``oracle.attention`` (on the CPU) the
+way a plausible bug would: a dropped scale, a transposed operand, a wrong
+causal offset, softmax over the wrong axis, a dropped term in the logsumexp, the
+wrong GQA head map, and the per-block normalisation of the tiled listing in the
+holysheep.ai article (section 2.2 "Tiling"), which divides by a block-local sum
+at every step and again at the end.  The pins of ``test_oracle_pins`` are then
+re-run against the mutated oracle; at least one of them must fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as A
+import test_oracle_pins as pins
+
+_orig = {n: getattr(A, n) for n in ("scores", "masked_softmax", "valid_mask", "kv_head", "tiled_fwd", "ref_bwd")}
+
+
+def _fwd_checks():
+    fwd = pins.fwd_oracle
+    return [lambda: pins.check_brute_force(fwd), lambda: pins.check_closed_forms(fwd),
+            lambda: pins.check_invariants(fwd), lambda: pins.check_chunked_equals_one_shot(fwd),
+            lambda: pins.check_torch_sdpa(fwd), pins.check_rows_sum_to_one]
+
+
+def _bwd_checks():
+    bwd = pins.bwd_oracle
+    return [lambda: pins.check_finite_differences(bwd), lambda: pins.check_gradient_identities(bwd),
+            lambda: pins.check_torch_autograd(bwd)]
+
+
+def _some_check_fails(checks):
+    for c in checks:
+        try:
+            if not c():
+                return True
+        except Exception:
+            return True
+    return False
+
+
+def _softmax_no_lse_max(S, mask):
+    P, m, lse = _orig["masked_softmax"](S, mask)
+    return P, m, np.where(np.isfinite(lse), lse - np.where(np.isfinite(m), m, 0), lse)
+
+
+def _softmax_wrong_axis(S, mask):
+    P, m, lse = _orig["masked_softmax"](S.T.copy(), mask.T.copy()) if S.shape[0] == S.shape[1] else \
+        _orig["masked_softmax"](S, mask)
+    if S.shape[0] == S.shape[1]:
+        return P.T.copy(), m, lse
+    # non-square: normalise columns instead of rows
+    E = np.where(mask, np.exp(S - S.max()), 0.0)
+    return E / np.maximum(E.sum(axis=0, keepdims=True), 1e-300), m, lse
+
+
+def _tiled_holysheep_bug(q2, k2, v2, block_q, block_k, causal=False, scale=None, dtype=np.float64):
+    """The article's per-block normalisation: O is divided by the current block's sum at each step."""
+    q2, k2, v2 = (np.asarray(x, dtype=dtype) for x in (q2, k2, v2))
+    Nq, d = q2.shape
+    Nk = k2.shape[0]
+    scale = scale if scale is not None else 1 / np.sqrt(d)
+    O = np.zeros((Nq, d)); L = np.zeros(Nq)
+    with np.errstate(all="ignore"):
+        return _holysheep_loop(q2, k2, v2, block_q, block_k, causal, scale, O, L, Nq, Nk, d)
+
+
+def _holysheep_loop(q2, k2, v2, block_q, block_k, causal, scale, O, L, Nq, Nk, d):
+    for i0 in range(0, Nq, block_q):
+        i1 = min(Nq, i0 + block_q)
+        Ob = np.zeros((i1 - i0, d)); mb = np.full(i1 - i0, -np.inf); lb = np.zeros(i1 - i0)
+        for j0 in range(0, Nk, block_k):
+            j1 = min(Nk, j0 + block_k)
+            S = (q2[i0:i1] @ k2[j0:j1].T) * scale
+            if causal:
+                S = np.where(np.arange(j0, j1)[None] <= np.arange(i0, i1)[:, None] + Nk - Nq, S, -np.inf)
+            mn = np.maximum(mb, S.max(axis=1))
+            Pb = np.exp(S - mn[:, None])
+            ln = Pb.sum(axis=1)
+            Ob = (np.exp(mb - mn)[:, None] * Ob + Pb @ v2[j0:j1]) / ln[:, None]
+            mb, lb = mn, ln
+        O[i0:i1] = Ob / lb[:, None]
+        L[i0:i1] = mb + np.log(lb)
+    return O, L
+
+
+def _bwd_no_delta(q, k, v, do, causal=False, scale=None, kv_lens=None):
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = scale if scale is not None else 1 / np.sqrt(d)
+    dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        mask = A.valid_mask(Nq, Nk, causal)
+        for h in range(Hq):
+            g = A.kv_head(h, Hq, Hkv)
+            P = A.masked_softmax(A.scores(q[b, h], k[b, g], scale), mask)[0]
+            dV[b, g] += P.T @ do[b, h]
+            dS = P * (do[b, h] @ v[b, g].T)          # D term dropped
+            dQ[b, h] = scale * (dS @ k[b, g])
+            dK[b, g] += scale * (dS.T @ q[b, h])
+    return dQ, dK, dV
+
+
+def _bwd_transposed_dv(q, k, v, do, causal=False, scale=None, kv_lens=None):
+    dQ, dK, dV = _orig["ref_bwd"](q, k, v, do, causal=causal, scale=scale)
+    q64, k64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, do))
+    B, Hq, Nq, d = q64.shape
+    Hkv, Nk = k64.shape[1], k64.shape[2]
+    scale = scale if scale is not None else 1 / np.sqrt(d)
+    dV = np.zeros_like(dV)
+    for b in range(B):
+        for h in range(Hq):
+            g = A.kv_head(h, Hq, Hkv)
+            P = A.masked_softmax(A.scores(q64[b, h], k64[b, g], scale), A.valid_mask(Nq, Nk, causal))[0]
+            dV[b, g] += (P @ do64[b, h]) if Nq == Nk else (P.T @ do64[b, h])[::-1]
+    return dQ, dK, dV
+
+
+def _bwd_unscaled_dk(q, k, v, do, causal=False, scale=None, kv_lens=None):
+    dQ, dK, dV = _orig["ref_bwd"](q, k, v, do, causal=causal, scale=scale)
+    s = scale if scale is not None else 1 / np.sqrt(np.shape(q)[-1])
+    return dQ, dK / s, dV
+
+
+FWD_MUTANTS = {
+    "scale_dropped": ("scores", lambda q, k, s: _orig["scores"](q, k, 1.0)),
+    "k_transposed_role": ("scores", lambda q, k, s: _orig["scores"](k, q, s).T if q.shape == k.shape
+                          else _orig["scores"](q, k[::-1], s)),
+    "causal_offset_sign": ("valid_mask", lambda Nq, Nk, c, kv=None: _orig["valid_mask"](Nq, Nk, False, kv) & (
+        (np.arange(Nk)[None] <= np.arange(Nq)[:, None] - (Nk - Nq)) if c else True)),
+    "causal_strict": ("valid_mask", lambda Nq, Nk, c, kv=None: _orig["valid_mask"](Nq, Nk, False, kv) & (
+        (np.arange(Nk)[None] < np.arange(Nq)[:, None] + (Nk - Nq)) | (np.arange(Nk)[None] == 0) if c else True)),
+    "lse_without_max": ("masked_softmax", _softmax_no_lse_max),
+    "softmax_wrong_axis": ("masked_softmax", _softmax_wrong_axis),
+    "gqa_modulo_map": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
+    "holysheep_block_normaliser": ("tiled_fwd", _tiled_holysheep_bug),
+}
+
+BWD_MUTANTS = {
+    "delta_term_dropped": ("ref_bwd", _bwd_no_delta),
+    "dv_transposed_operand": ("ref_bwd", _bwd_transposed_dv),
+    "dk_scale_dropped": ("ref_bwd", _bwd_unscaled_dk),
+}
+
+
+def test_unmutated_oracle_passes_every_check():
+    assert not _some_check_fails(_fwd_checks())
+    assert not _some_check_fails(_bwd_checks())
+
+
+@pytest.mark.parametrize("name", sorted(FWD_MUTANTS))
+def test_forward_mutant_is_caught(name, monkeypatch):
+    attr, fn = FWD_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    if attr == "tiled_fwd":
+        monkeypatch.setattr(oracle, "tiled_fwd", fn)
+    assert _some_check_fails(_fwd_checks()), f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, monkeypatch):
+    attr, fn = BWD_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    assert _some_check_fails(_bwd_checks()), f"mutant {name} passed every pin"

@@ -1,0 +1,67 @@
+"""The seeded input generators: determinism, recipe, and bf16 rounding."""
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def test_bf16_rounding_matches_torch_rne():
+    g = np.random.default_rng(1)
+    x = np.concatenate([g.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 65504.0, 3.0e38, -3.0e38, 1e-40, np.inf, -np.inf],
+                                 dtype=np.float32)])
+    # ties: values exactly halfway between two bf16 numbers
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    ours = W.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = W.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+    assert np.isnan(W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.array([np.nan], np.float32))))[0]
+
+
+def test_generators_are_deterministic_and_seeded():
+    a = W.make_config(2, B=1, Hq=2, Hkv=2, Nq=64, Nk=64)
+    b = W.make_config(2, B=1, Hq=2, Hkv=2, Nq=64, Nk=64)
+    for n in ("q", "k", "v"):
+        assert np.array_equal(a.tensors[n], b.tensors[n])
+    assert not np.array_equal(a.tensors["q"], a.tensors["k"])
+    c = W.make_config(3, B=1, Hq=2, Hkv=2, Nq=64, Nk=64)
+    assert not np.array_equal(a.tensors["q"], c.tensors["q"])
+
+
+def test_config_recipes():
+    w1 = W.make_config(1)
+    assert w1.tensors["q"].dtype == np.float32 and w1.tensors["q"].shape == (1, 1, 256, 64)
+    assert not w1.causal and abs(w1.scale - 0.125) < 1e-15
+    w3 = W.make_config(3, B=1, Hq=2, Hkv=2, Nq=1000, Nk=1000)
+    # 1% of K rows per (b, h) scaled by 8 (exact in bf16): compare with the unscaled draw
+    raw = W.normal_bf16_bits(W.rng(3, W.STREAM_K), (1, 2, 1000, 128))
+    kv, rv = W.bf16_bits_to_f32(w3.tensors["k"]), W.bf16_bits_to_f32(raw)
+    for h in range(2):
+        rows = w3.outlier_rows[0, h]
+        assert len(rows) == 10 and len(set(rows.tolist())) == 10
+        assert np.array_equal(kv[0, h, rows], 8 * rv[0, h, rows])
+        others = np.setdiff1d(np.arange(1000), rows)
+        assert np.array_equal(kv[0, h, others], rv[0, h, others])
+    assert w3.sample_rows.shape == (512, 3)
+    assert len({tuple(r) for r in w3.sample_rows.tolist()}) == 512
+    w4 = W.make_config(4, B=16, Hq=4, Hkv=1, Nk=2048, len_lo=100)
+    assert w4.seqlens.dtype == np.int32 and w4.seqlens.min() >= 100 and w4.seqlens.max() <= 2048
+    full = W.make_config.__wrapped__ if hasattr(W.make_config, "__wrapped__") else None
+    assert full is None
+    w5 = W.make_config(5, B=1, Hq=1, Hkv=1, Nq=64, Nk=64)
+    assert "do" in w5.tensors and w5.causal
+
+
+def test_full_decode_lengths_recipe():
+    lens = W.cache_lengths(4, 16, 4096, 32768)
+    assert lens.min() >= 4096 and lens.max() <= 32768
+    assert np.array_equal(lens, W.cache_lengths(4, 16, 4096, 32768))
+
+
+def test_values_are_normal():
+    w = W.make_config(2, B=1, Hq=4, Hkv=4, Nq=2048, Nk=2048)
+    x = w.values("q").astype(np.float64)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
