@@ -1,0 +1,189 @@
+"""Python binding of libfa (exact IO-aware attention on MI355X / gfx950).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed to
+the C ABI (``include/fa.h``), and a non-zero status raises ``RuntimeError``.
+Every step of the computation runs in the HIP kernels of ``libfa.so``; there is
+no fallback of any kind.  PyTorch only provides device memory and streams.
+
+Low-level entry points mirror the C names (``fa_fwd``, ``fa_bwd``,
+``fa_decode``, ``fa_bwd_workspace_bytes``, ``fa_decode_workspace_bytes``) and
+write into caller-provided tensors.  ``fwd``, ``bwd`` and ``decode`` allocate
+their outputs with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F32, FA_BF16 = 0, 1
+FA_OK = 0
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_16_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_abi_version.restype = i
+    lib.fa_abi_version.argtypes = []
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode.restype = i
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise RuntimeError(load_library().fa_status_str(status).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _dev(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# C-ABI mirrors
+# ---------------------------------------------------------------------------
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def fa_bwd_workspace_bytes(B, Hq, Nq, d) -> int:
+    return load_library().fa_bwd_workspace_bytes(B, Hq, Nq, d)
+
+
+def fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d) -> int:
+    return load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)
+
+
+def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
+    """O = softmax(scale Q K^T [+causal]) V into ``o``; row logsumexp into ``lse``."""
+    _dev(q, k, v, o, lse)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                 _dtype_code(q), scale, int(bool(causal)), _stream(stream)))
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
+    """Gradients of sum(O * dO) into dq, dk, dv (their dtype picks the gradient dtype)."""
+    _dev(q, k, v, o, dO, lse, dq, dk, dv, workspace)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    gcode = _dtype_code(dq)
+    if _dtype_code(dk) != gcode or _dtype_code(dv) != gcode:
+        raise TypeError("dq, dk, dv must share one dtype")
+    _check(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), gcode, B, Hq, Hkv, Nq, Nk, d, _dtype_code(q), scale,
+                                 int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
+    """One query token per head against the first seqlens[b] cached keys."""
+    _dev(q, k_cache, v_cache, seqlens, o, lse, workspace)
+    torch = _torch()
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    B, Hq, _, d = q.shape
+    _, Hkv, Nmax, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(load_library().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
+                                    B, Hq, Hkv, Nmax, d, _dtype_code(q), scale, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences (outputs allocated by torch, computed by libfa)
+# ---------------------------------------------------------------------------
+
+def fwd(q, k, v, causal=False, scale=None, stream=None):
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)
+    return o, lse
+
+
+def bwd(q, k, v, o, dO, lse, causal=False, scale=None, grad_dtype=None, stream=None):
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    gd = torch.float32 if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, Hq, Nq, d)), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, ws, causal=causal, scale=scale, stream=stream)
+    return dq, dk, dv
+
+
+def decode_workspace(q, k_cache):
+    torch = _torch()
+    B, Hq, _, d = q.shape
+    _, Hkv, Nmax, _ = k_cache.shape
+    return torch.empty(max(1, fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)), dtype=torch.uint8,
+                       device=q.device)
+
+
+def decode(q, k_cache, v_cache, seqlens, scale=None, workspace=None, stream=None):
+    torch = _torch()
+    B, Hq, _, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = decode_workspace(q, k_cache) if workspace is None else workspace
+    fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale=scale, stream=stream)
+    return o, lse

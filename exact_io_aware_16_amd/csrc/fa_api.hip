@@ -1,0 +1,124 @@
+// C ABI of libfa (declared in include/fa.h): argument validation, workspace
+// sizing and launch.  Every check happens on the host before anything is
+// enqueued; the library keeps no state between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 31;
+
+bool too_big(int64_t a, int64_t b, int64_t c, int64_t d) { return a * b * c * d >= kMaxElems; }
+
+fa_status_t check_scale(float scale) {
+    return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_ARG;
+}
+
+fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+size_t decode_nsplit(int Nmax) { return (size_t)((Nmax + fa::kDecodeSplit - 1) / fa::kDecodeSplit); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (size < 1, Hq % Hkv != 0, causal with Nq > Nk, or tensor too large)";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+        case FA_ERR_ARG: return "FA_ERR_ARG: scale must be finite and > 0, pointers 16-byte aligned";
+        default: return "unknown fa status";
+    }
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, fa_dtype_t dtype, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (causal && Nq > Nk) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, Nq, d) || too_big(B, Hkv, Nk, d)) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ARG;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, stream};
+    return from_hip(dtype == FA_BF16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a, nullptr));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d) {
+    (void)d;
+    if (B < 1 || Hq < 1 || Nq < 1) return 0;
+    return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, fa_dtype_t grad_dtype, int B, int Hq, int Hkv, int Nq, int Nk,
+                   int d, fa_dtype_t dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (causal && Nq > Nk) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, Nq, d) || too_big(B, Hkv, Nk, d)) return FA_ERR_SHAPE;
+    if ((dtype != FA_F32 && dtype != FA_BF16) || (grad_dtype != FA_F32 && grad_dtype != FA_BF16))
+        return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned4(lse) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return FA_ERR_ARG;
+    fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, grad_dtype == FA_BF16 ? 1 : 0, B, Hq, Hkv, Nq, Nk, d,
+                  scale, causal ? 1 : 0, static_cast<float*>(workspace), stream};
+    return from_hip(dtype == FA_BF16 ? fa::launch_bwd_bf16(a) : fa::launch_bwd_f32(a));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d) {
+    (void)Hkv;
+    if (B < 1 || Hq < 1 || Nmax < 1 || d < 1) return 0;
+    const size_t rows = (size_t)B * Hq * decode_nsplit(Nmax);
+    return rows * (size_t)d * sizeof(float) + rows * sizeof(float);
+}
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Nmax, int d, fa_dtype_t dtype, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nmax < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, 1, d) || too_big(B, Hkv, Nmax, d)) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)) return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(seqlens) || !aligned16(o) ||
+        !aligned4(lse) || !aligned16(workspace))
+        return FA_ERR_ARG;
+    if (dtype == FA_F32) {
+        // float32: the forward kernel with per-sequence key limits (one query row)
+        fa::FwdArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, 1, Nmax, d, scale, 0, stream};
+        return from_hip(fa::launch_fwd_f32(a, seqlens));
+    }
+    const size_t nsplit = decode_nsplit(Nmax);
+    float* part_o = static_cast<float*>(workspace);
+    float* part_lse = part_o + (size_t)B * Hq * nsplit * d;
+    fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nmax, d, scale, part_o, part_lse,
+                     (int)nsplit, stream};
+    return from_hip(fa::launch_decode_bf16(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,636 @@
+// Backward pass of exact attention on gfx950.
+//
+// Recomputation (thienlv.com glossary "Flash Attention Là Gì?", section "Ba Kỹ
+// Thuật Chính", item 2): P is never stored by the forward pass; the backward
+// rebuilds it tile by tile from Q, K and the saved row logsumexp,
+// P_ij = exp(scale q_i.k_j - lse_i), and then applies the chain rule of
+// O = P V, P = softmax(scale Q K^T):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D) with D_i = dO_i . O_i,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// MI355X mapping.  Three kernels on one stream, no atomics, so the result is
+// bitwise reproducible:
+//  1. bwd_delta: D_i = dO_i . O_i in float32 (one row per 16 lanes).
+//  2. bwd_dq (query owner, shaped like the forward pass): each wave owns 32
+//     query rows; S^T = K Q^T and dP^T = V dO^T put one query per lane, so
+//     lse_i and D_i are per-lane scalars; dQ^T += K^T dS^T accumulates in
+//     registers (K is staged twice in LDS: as is, and transposed + key-permuted
+//     so a lane's eight keys are contiguous).
+//  3. bwd_dkdv (key owner): each wave owns 32 keys for the whole pass, K and V
+//     rows sit in registers, and for every query head of the group and every
+//     query block S = Q K^T and dP = dO V^T put one key per lane; then
+//     dV^T += dO^T P and dK^T += Q^T dS accumulate in registers (Q and dO are
+//     staged as is and transposed).  Grouped heads are summed in registers.
+// The key-owner kernel recomputes S and dP that the query-owner kernel also
+// computes (7 matrix products instead of 5); that buys determinism and removes
+// every atomic read-modify-write of dQ.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+// Same permutation as the forward pass: key kappa of a 32-key group lands at
+// the slot where a lane half finds its eight keys contiguously, in the order
+// its score registers hold them.
+__device__ __forceinline__ int perm32(int kappa) {
+    const int mt = kappa >> 5, g = (kappa >> 3) & 3, hh = (kappa >> 2) & 1;
+    return mt * 32 + (g >> 1) * 16 + hh * 8 + (g & 1) * 4;
+}
+
+// Loads four consecutive rows (clamped to row_end - 1) of an 8-column chunk.
+template <int D>
+__device__ __forceinline__ void load4(u32x4 (&r)[4], const uint16_t* __restrict__ base, int row0, int row_end,
+                                      int c8) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = min(row0 + u, row_end - 1);
+        r[u] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + c8 * 8);
+    }
+}
+
+// Writes four rows as is (stride S) and transposed (stride TS, permuted slot).
+template <int S, int TS>
+__device__ __forceinline__ void store4(const u32x4 (&r)[4], uint16_t* nat, uint16_t* tr, int row0, int c8) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(nat + (row0 + u) * S + c8 * 8) = r[u];
+    if (tr) {
+        const int pos = perm32(row0);
+        static_for<0, 8>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            *reinterpret_cast<u32x2*>(tr + (c8 * 8 + e) * TS + pos) =
+                u32x2{pack_col<e>(r[0], r[1]), pack_col<e>(r[2], r[3])};
+        });
+    }
+}
+
+__device__ __forceinline__ void store_grad4(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void store_grad4(uint16_t* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. D_i = dO_i . O_i
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const uint16_t* __restrict__ O,
+                                                             const uint16_t* __restrict__ dO,
+                                                             float* __restrict__ delta, int rows) {
+    constexpr int LPR = D / 8;  // lanes per row
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int row = t / LPR, c8 = t % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + c8 * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + c8 * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = __builtin_fmaf(bf16_bits_to_f32(a[w] & 0xffffu), bf16_bits_to_f32(b[w] & 0xffffu), acc);
+            acc = __builtin_fmaf(bf16_bits_to_f32(a[w] >> 16), bf16_bits_to_f32(b[w] >> 16), acc);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && c8 == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dQ, query owner
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqTile {
+    static constexpr int BM = 128;       // queries per workgroup (4 waves x 32)
+    static constexpr int BN = 32;        // keys per block
+    static constexpr int KS = D + 8;     // K / V row stride
+    static constexpr int TS = BN + 8;    // K^T row stride
+    static constexpr int K_EL = BN * KS, KT_EL = D * TS, V_EL = BN * KS;
+    static constexpr int STAGE = K_EL + KT_EL + V_EL;
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int KIT = (BN / 4) * (D / 8);     // 4-row items for K (threads 0..KIT-1)
+    static constexpr int VCH = BN * D / 8;             // 16-byte chunks of V
+    static constexpr int VPT = VCH / (256 - KIT);      // per thread for threads KIT..255
+};
+
+template <int D, bool CAUSAL, typename G>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    G* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH, float sl2, float scale) {
+    using T = DqTile<D>;
+    extern __shared__ __align__(16) uint16_t smem[];
+    const int id = blockIdx.x;
+    const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
+    const int bh = id % BH;
+    const int b = bh / Hq, h = bh % Hq;
+    const int hk = h / (Hq / Hkv);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+    const int off = Nk - Nq;
+    const int qw = qb * T::BM + wave * 32;
+    const int qi = qw + n;
+    const int qc = min(qi, Nq - 1);
+    const size_t qrow = (size_t)(b * Hq + h) * Nq + qc;
+
+    bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q + qrow * D + kk * 16 + hf * 8));
+        df[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dO + qrow * D + kk * 16 + hf * 8));
+    }
+    const float lse_v = LSE[qrow];
+    // rows with no visible key (lse = -inf) get P = 0
+    const float lse2 = lse_v == kNegInf ? __builtin_huge_valf() : lse_v * kLog2e;
+    const float dlt = delta[qrow];
+
+    const uint16_t* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
+    const uint16_t* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
+    const int nblk = (kv_end + T::BN - 1) / T::BN;
+    const int wave_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) acc[md] = zero16();
+
+    u32x4 kr[4], vr[T::VPT];
+    auto load = [&](int key0) {
+        if (tid < T::KIT) {
+            const int kq = tid / (D / 8), c8 = tid % (D / 8);
+            load4<D>(kr, kb, key0 + kq * 4, kv_end, c8);
+        } else {
+#pragma unroll
+            for (int r = 0; r < T::VPT; ++r) {
+                const int c = (tid - T::KIT) + (256 - T::KIT) * r;
+                const int row = c / (D / 8), c8 = c % (D / 8);
+                const int key = min(key0 + row, kv_end - 1);
+                vr[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c8 * 8);
+            }
+        }
+    };
+    auto store = [&](uint16_t* st) {
+        if (tid < T::KIT) {
+            const int kq = tid / (D / 8), c8 = tid % (D / 8);
+            store4<T::KS, T::TS>(kr, st, st + T::K_EL, kq * 4, c8);
+        } else {
+            uint16_t* sV = st + T::K_EL + T::KT_EL;
+#pragma unroll
+            for (int r = 0; r < T::VPT; ++r) {
+                const int c = (tid - T::KIT) + (256 - T::KIT) * r;
+                const int row = c / (D / 8), c8 = c % (D / 8);
+                *reinterpret_cast<u32x4*>(sV + row * T::KS + c8 * 8) = vr[r];
+            }
+        }
+    };
+
+    load(0);
+    store(smem);
+    __syncthreads();
+    for (int j = 0; j < nblk; ++j) {
+        const int key0 = j * T::BN;
+        uint16_t* st = smem + (j & 1) * T::STAGE;
+        if (j + 1 < nblk) load(key0 + T::BN);
+        if (key0 < wave_end) {
+            const uint16_t* sK = st;
+            const uint16_t* sKT = st + T::K_EL;
+            const uint16_t* sV = st + T::K_EL + T::KT_EL;
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sK + n * T::KS + kk * 16 + hf * 8), qf[kk], s);
+                dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sV + n * T::KS + kk * 16 + hf * 8), df[kk], dp);
+            }
+            const bool need_mask = key0 + T::BN > kv_end || (CAUSAL && key0 + T::BN > qw + off);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float p = exp2_fast(__builtin_fmaf(s[i], sl2, -lse2));
+                if (need_mask) {
+                    const int key = key0 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                    const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
+                    p = ok ? p : 0.f;
+                }
+                s[i] = p * (dp[i] - dlt);  // dS^T
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 db;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) db[e] = (__bf16)s[ks * 8 + e];
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md)
+                    acc[md] = mfma32x32x16(
+                        *reinterpret_cast<const bf16x8*>(sKT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), db, acc[md]);
+            }
+        }
+        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * T::STAGE);
+        __syncthreads();
+    }
+    if (qi < Nq) {
+        G* out = dQ + ((size_t)(b * Hq + h) * Nq + qi) * D;
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store_grad4(out + md * 32 + g * 8 + hf * 4, acc[md][g * 4] * scale, acc[md][g * 4 + 1] * scale,
+                            acc[md][g * 4 + 2] * scale, acc[md][g * 4 + 3] * scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK, dV, key owner
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkvTile {
+    static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
+    static constexpr int BQ = 32;        // queries per block
+    static constexpr int RS = D + 8;     // Q / dO row stride
+    static constexpr int TS = BQ + 8;    // Q^T / dO^T row stride
+    static constexpr int NAT = BQ * RS, TR = D * TS;
+    static constexpr int STAGE = 2 * NAT + 2 * TR + 2 * BQ * 2;  // + lse2 and delta (float = 2 elems)
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int IT = (BQ / 4) * (D / 8);  // 4-row items per tensor
+};
+
+template <int D, bool CAUSAL, typename G>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    G* __restrict__ dK, G* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkb, float sl2, float scale) {
+    using T = DkvTile<D>;
+    extern __shared__ __align__(16) uint16_t smem[];
+    const int id = blockIdx.x;
+    // key blocks near the start see the most queries under the causal mask: issue them first
+    const int kblk = id % nkb;
+    const int bhk = id / nkb;
+    const int b = bhk / Hkv, hk = bhk % Hkv;
+    const int g = Hq / Hkv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+    const int off = Nk - Nq;
+    const int kw = kblk * T::BK + wave * 32;   // first key of this wave
+    const int kj = kw + n;
+    const int kc = min(kj, Nk - 1);
+    const size_t krow = (size_t)(b * Hkv + hk) * Nk + kc;
+
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(K + krow * D + kk * 16 + hf * 8));
+        vf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(V + krow * D + kk * 16 + hf * 8));
+    }
+
+    f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+        dv[md] = zero16();
+        dk[md] = zero16();
+    }
+
+    // first query that sees any key of this workgroup / wave
+    const int q_begin = CAUSAL ? max(0, kblk * T::BK - off) : 0;
+    const int qb0 = q_begin / T::BQ;
+    const int nqblk = (Nq + T::BQ - 1) / T::BQ - qb0;
+    const int total = g * nqblk;   // (head, query block) steps
+    const int wave_q_begin = CAUSAL ? max(0, kw - off) : 0;
+
+    u32x4 rr[4];
+    float aux = 0.f;
+    auto load = [&](int step) {
+        const int hq = hk * g + step / nqblk;
+        const int q0 = (qb0 + step % nqblk) * T::BQ;
+        const size_t base = (size_t)(b * Hq + hq) * Nq;
+        if (tid < 2 * T::IT) {
+            const int t = tid % T::IT;
+            const int kq = t / (D / 8), c8 = t % (D / 8);
+            load4<D>(rr, (tid < T::IT ? Q : dO) + base * D, q0 + kq * 4, Nq, c8);
+        }
+        const int lt = tid - 2 * T::IT;
+        if (lt >= 0 && lt < 2 * T::BQ) {
+            const int qrow = min(q0 + (lt % T::BQ), Nq - 1);
+            if (lt < T::BQ) {
+                const float l = LSE[base + qrow];
+                aux = (q0 + lt < Nq && l != kNegInf) ? l * kLog2e : __builtin_huge_valf();
+            } else {
+                aux = delta[base + qrow];
+            }
+        }
+    };
+    auto store = [&](uint16_t* st) {
+        if (tid < 2 * T::IT) {
+            const int t = tid % T::IT;
+            const int kq = t / (D / 8), c8 = t % (D / 8);
+            uint16_t* nat = st + (tid < T::IT ? 0 : T::NAT);
+            uint16_t* tr = st + 2 * T::NAT + (tid < T::IT ? 0 : T::TR);
+            store4<T::RS, T::TS>(rr, nat, tr, kq * 4, c8);
+        }
+        const int lt = tid - 2 * T::IT;
+        if (lt >= 0 && lt < 2 * T::BQ) reinterpret_cast<float*>(st + 2 * T::NAT + 2 * T::TR)[lt] = aux;
+    };
+
+    if (total > 0) {
+        load(0);
+        store(smem);
+    }
+    __syncthreads();
+    for (int stp = 0; stp < total; ++stp) {
+        const int q0 = (qb0 + stp % nqblk) * T::BQ;
+        uint16_t* st = smem + (stp & 1) * T::STAGE;
+        if (stp + 1 < total) load(stp + 1);
+        if (q0 + T::BQ > wave_q_begin && kw < Nk) {
+            const uint16_t* sQ = st;
+            const uint16_t* sdO = st + T::NAT;
+            const uint16_t* sQT = st + 2 * T::NAT;
+            const uint16_t* sdOT = sQT + T::TR;
+            const float* sL = reinterpret_cast<const float*>(sdOT + T::TR);
+            const float* sD = sL + T::BQ;
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sQ + n * T::RS + kk * 16 + hf * 8), kf[kk], s);
+                dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sdO + n * T::RS + kk * 16 + hf * 8), vf[kk], dp);
+            }
+            const bool need_mask = kw + 32 > Nk || (CAUSAL && kw + 31 > q0 + off);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int r0 = gq * 8 + hf * 4;   // query rows r0..r0+3 of this block
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + r0);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = gq * 4 + r;
+                    float p = exp2_fast(__builtin_fmaf(s[i], sl2, -l4[r]));
+                    if (need_mask) {
+                        const bool ok = kj < Nk && (!CAUSAL || kj <= q0 + r0 + r + off);
+                        p = ok ? p : 0.f;
+                    }
+                    s[i] = p;
+                    dp[i] = p * (dp[i] - d4[r]);   // dS
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 pb, db;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pb[e] = (__bf16)s[ks * 8 + e];
+                    db[e] = (__bf16)dp[ks * 8 + e];
+                }
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md) {
+                    dv[md] = mfma32x32x16(
+                        *reinterpret_cast<const bf16x8*>(sdOT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), pb, dv[md]);
+                    dk[md] = mfma32x32x16(
+                        *reinterpret_cast<const bf16x8*>(sQT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), db, dk[md]);
+                }
+            }
+        }
+        if (stp + 1 < total) store(smem + ((stp + 1) & 1) * T::STAGE);
+        __syncthreads();
+    }
+    if (kj < Nk) {
+        const size_t o = ((size_t)(b * Hkv + hk) * Nk + kj) * D;
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const int dcol = md * 32 + gg * 8 + hf * 4;
+                store_grad4(dK + o + dcol, dk[md][gg * 4] * scale, dk[md][gg * 4 + 1] * scale,
+                            dk[md][gg * 4 + 2] * scale, dk[md][gg * 4 + 3] * scale);
+                store_grad4(dV + o + dcol, dv[md][gg * 4], dv[md][gg * 4 + 1], dv[md][gg * 4 + 2], dv[md][gg * 4 + 3]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// float32 backward on the vector ALUs, four lanes per row (d/4 columns each)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
+                                                            float* __restrict__ delta, int rows) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int row = t >> 2, part = t & 3;
+    float acc = 0.f;
+    if (row < rows) {
+        const float* a = O + (size_t)row * D + part * (D / 4);
+        const float* c = dO + (size_t)row * D + part * (D / 4);
+        for (int i = 0; i < D / 4; ++i) acc = __builtin_fmaf(a[i], c[i], acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (row < rows && part == 0) delta[row] = acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                         const float* __restrict__ V, const float* __restrict__ dO,
+                                                         const float* __restrict__ LSE,
+                                                         const float* __restrict__ delta, float* __restrict__ dQ,
+                                                         int Hq, int Hkv, int Nq, int Nk, int causal, float sl2,
+                                                         float scale) {
+    constexpr int DS = D / 4, BK = 32;
+    __shared__ float sK[BK][D + 4];
+    __shared__ float sV[BK][D + 4];
+    const int b = blockIdx.z, h = blockIdx.y, hk = h / (Hq / Hkv);
+    const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+    const int qi = blockIdx.x * 64 + row;
+    const int off = Nk - Nq;
+    const size_t qr = (size_t)(b * Hq + h) * Nq + min(qi, Nq - 1);
+    float q[DS], d_o[DS], dq[DS];
+#pragma unroll
+    for (int c = 0; c < DS; ++c) {
+        q[c] = Q[qr * D + part * DS + c];
+        d_o[c] = dO[qr * D + part * DS + c];
+        dq[c] = 0.f;
+    }
+    const float l = LSE[qr];
+    const float lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    const float dl = delta[qr];
+    const float* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
+    const float* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
+    int end = Nk;
+    if (causal) end = min(Nk, blockIdx.x * 64 + 64 + off);
+    for (int key0 = 0; key0 < end; key0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < BK * D; e += 256) {
+            const int r = e / D, c = e % D;
+            const int key = min(key0 + r, Nk - 1);
+            sK[r][c] = kb[(size_t)key * D + c];
+            sV[r][c] = vb[(size_t)key * D + c];
+        }
+        __syncthreads();
+        for (int j = 0; j < BK; ++j) {
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int c = 0; c < DS; ++c) {
+                s = __builtin_fmaf(q[c], sK[j][part * DS + c], s);
+                dp = __builtin_fmaf(d_o[c], sV[j][part * DS + c], dp);
+            }
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            dp += __shfl_xor(dp, 1, 64);
+            dp += __shfl_xor(dp, 2, 64);
+            const int key = key0 + j;
+            const bool ok = key < Nk && (!causal || key <= qi + off);
+            const float p = ok ? exp2_fast(__builtin_fmaf(s, sl2, -lse2)) : 0.f;
+            const float ds = p * (dp - dl);
+#pragma unroll
+            for (int c = 0; c < DS; ++c) dq[c] = __builtin_fmaf(ds, sK[j][part * DS + c], dq[c]);
+        }
+    }
+    if (qi < Nq) {
+#pragma unroll
+        for (int c = 0; c < DS; ++c) dQ[qr * D + part * DS + c] = dq[c] * scale;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                           const float* __restrict__ V, const float* __restrict__ dO,
+                                                           const float* __restrict__ LSE,
+                                                           const float* __restrict__ delta, float* __restrict__ dK,
+                                                           float* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk,
+                                                           int causal, float sl2, float scale) {
+    constexpr int DS = D / 4, BQ = 32;
+    __shared__ float sQ[BQ][D + 4];
+    __shared__ float sdO[BQ][D + 4];
+    __shared__ float sL[BQ], sD[BQ];
+    const int b = blockIdx.z, hk = blockIdx.y, g = Hq / Hkv;
+    const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+    const int kj = blockIdx.x * 64 + row;
+    const int off = Nk - Nq;
+    const size_t kr = (size_t)(b * Hkv + hk) * Nk + min(kj, Nk - 1);
+    float k[DS], v[DS], dk[DS], dv[DS];
+#pragma unroll
+    for (int c = 0; c < DS; ++c) {
+        k[c] = K[kr * D + part * DS + c];
+        v[c] = V[kr * D + part * DS + c];
+        dk[c] = 0.f;
+        dv[c] = 0.f;
+    }
+    const int q_begin = causal ? max(0, (int)blockIdx.x * 64 - off) : 0;
+    for (int hq = hk * g; hq < hk * g + g; ++hq) {
+        const size_t base = (size_t)(b * Hq + hq) * Nq;
+        for (int q0 = (q_begin / BQ) * BQ; q0 < Nq; q0 += BQ) {
+            __syncthreads();
+            for (int e = tid; e < BQ * D; e += 256) {
+                const int r = e / D, c = e % D;
+                const int qq = min(q0 + r, Nq - 1);
+                sQ[r][c] = Q[(base + qq) * D + c];
+                sdO[r][c] = dO[(base + qq) * D + c];
+            }
+            if (tid < BQ) {
+                const int qq = min(q0 + tid, Nq - 1);
+                const float l = LSE[base + qq];
+                sL[tid] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+                sD[tid] = delta[base + qq];
+            }
+            __syncthreads();
+            for (int i = 0; i < BQ; ++i) {
+                float s = 0.f, dp = 0.f;
+#pragma unroll
+                for (int c = 0; c < DS; ++c) {
+                    s = __builtin_fmaf(sQ[i][part * DS + c], k[c], s);
+                    dp = __builtin_fmaf(sdO[i][part * DS + c], v[c], dp);
+                }
+                s += __shfl_xor(s, 1, 64);
+                s += __shfl_xor(s, 2, 64);
+                dp += __shfl_xor(dp, 1, 64);
+                dp += __shfl_xor(dp, 2, 64);
+                const int qi = q0 + i;
+                const bool ok = qi < Nq && kj < Nk && (!causal || kj <= qi + off);
+                const float p = ok ? exp2_fast(__builtin_fmaf(s, sl2, -sL[i])) : 0.f;
+                const float ds = p * (dp - sD[i]);
+#pragma unroll
+                for (int c = 0; c < DS; ++c) {
+                    dv[c] = __builtin_fmaf(p, sdO[i][part * DS + c], dv[c]);
+                    dk[c] = __builtin_fmaf(ds, sQ[i][part * DS + c], dk[c]);
+                }
+            }
+        }
+    }
+    if (kj < Nk) {
+#pragma unroll
+        for (int c = 0; c < DS; ++c) {
+            dK[kr * D + part * DS + c] = dk[c] * scale;
+            dV[kr * D + part * DS + c] = dv[c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, typename G>
+static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
+    const hipStream_t s = (hipStream_t)a.stream;
+    const int rows = a.B * a.Hq * a.Nq;
+    hipLaunchKernelGGL(bwd_delta_bf16_kernel<D>, dim3((rows * (D / 8) + 255) / 256), dim3(256), 0, s,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dO, a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float sl2 = a.scale * kLog2e;
+    {
+        using T = DqTile<D>;
+        const int nqb = (a.Nq + T::BM - 1) / T::BM;
+        const int BH = a.B * a.Hq;
+        auto kern = bwd_dq_kernel<D, CAUSAL, G>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                T::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
+                           (G*)a.dq, a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, sl2, a.scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        using T = DkvTile<D>;
+        const int nkb = (a.Nk + T::BK - 1) / T::BK;
+        auto kern = bwd_dkdv_kernel<D, CAUSAL, G>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                T::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(nkb * a.B * a.Hkv), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
+                           (G*)a.dk, (G*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, nkb, sl2, a.scale);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
+    if (a.grad_bf16)
+        return a.causal ? launch_bwd_bf16_t<D, true, uint16_t>(a) : launch_bwd_bf16_t<D, false, uint16_t>(a);
+    return a.causal ? launch_bwd_bf16_t<D, true, float>(a) : launch_bwd_bf16_t<D, false, float>(a);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) { return a.d == 64 ? launch_bwd_bf16_d<64>(a) : launch_bwd_bf16_d<128>(a); }
+
+template <int D>
+static hipError_t launch_bwd_f32_d(const BwdArgs& a) {
+    const hipStream_t s = (hipStream_t)a.stream;
+    const int rows = a.B * a.Hq * a.Nq;
+    hipLaunchKernelGGL(bwd_delta_f32_kernel<D>, dim3((rows * 4 + 255) / 256), dim3(256), 0, s, (const float*)a.o,
+                       (const float*)a.dO, a.delta, rows);
+    const float sl2 = a.scale * kLog2e;
+    hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3((a.Nq + 63) / 64, a.Hq, a.B), dim3(256), 0, s, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.dO, a.lse, a.delta, (float*)a.dq, a.Hq,
+                       a.Hkv, a.Nq, a.Nk, a.causal, sl2, a.scale);
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3((a.Nk + 63) / 64, a.Hkv, a.B), dim3(256), 0, s,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO, a.lse, a.delta,
+                       (float*)a.dk, (float*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, a.causal, sl2, a.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a) {
+    // float32 gradients only for float32 inputs
+    if (a.grad_bf16) return hipErrorNotSupported;
+    return a.d == 64 ? launch_bwd_f32_d<64>(a) : launch_bwd_f32_d<128>(a);
+}
+
+}  // namespace fa

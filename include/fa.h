@@ -1,0 +1,130 @@
+/*
+ * fa.h — C ABI of libfa: exact scaled-dot-product attention on AMD Instinct
+ * MI355X (gfx950), computed tile by tile with the online-softmax recurrence so
+ * that the N x N score matrix never reaches device memory.
+ *
+ * Definition (handsonai.io "DL101 chapter 9", section 1.1 Key/Value Caching):
+ *   O = softmax(scale * Q K^T [+ causal mask]) V,   scale normally 1/sqrt(d).
+ * Recurrence (same page, section 3.3 FlashAttention; holysheep.ai Flash
+ * Attention article, section 2.1 Online Softmax): a running row max m and
+ * denominator l; when a new K/V block arrives the partial output and l are
+ * rescaled by exp(m_old - m_new); one division by l at the end.
+ * Backward (thienlv.com glossary "Flash Attention Là Gì?", section "Ba Kỹ Thuật
+ * Chính", item 2): P is recomputed from Q, K and the saved logsumexp instead of
+ * being stored.
+ * Grouped K/V heads (DL101 chapter 9, sections 3.1 MQA and 3.2 GQA): query head
+ * h reads K/V head h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to a contiguous row-major tensor,
+ *   head dimension fastest: q/o/dq/do are [B][Hq][Nq][d]; k/v/dk/dv are
+ *   [B][Hkv][Nk][d]; lse is [B][Hq][Nq] float32.
+ * - dtype FA_BF16: q, k, v, o, do are bfloat16 (raw 16-bit storage); the
+ *   kernels compute QK^T and PV on bf16 matrix cores with float32 accumulation
+ *   and keep the softmax statistics in float32.  FA_F32: all of them are
+ *   float32 and every step is float32.
+ * - lse (logsumexp) of query row i is the natural log of sum_j exp(scale *
+ *   q_i . k_j) over the keys row i may see.  A row that sees no key gets
+ *   O = 0 and lse = -inf.
+ * - causal != 0: key j is visible to query i iff j <= i + (Nk - Nq)
+ *   (bottom-right aligned; equal to the lower triangle when Nq == Nk).
+ *   Causal with Nq > Nk is rejected (rows without keys would be the norm).
+ * - d must be 64 or 128.  Hq must be a multiple of Hkv.  All sizes >= 1 unless
+ *   stated.  Tensor sizes are limited to 2^31 elements each.
+ * - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on that stream and returns; nothing is synchronised.
+ * - Ownership: the caller allocates and owns every buffer, workspaces
+ *   included.  The library allocates nothing, frees nothing, keeps no pointer
+ *   after returning, and holds no mutable global state, so calls on different
+ *   streams are independent.  Outputs are fully overwritten.
+ * - Errors: host-visible arguments are checked before anything is enqueued;
+ *   on any error nothing is launched and a status != FA_OK is returned.  A
+ *   failed kernel launch returns FA_ERR_HIP.  No exception crosses the ABI.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                      */
+    FA_ERR_SHAPE = 2,        /* a size < 1, Hq % Hkv != 0, causal with Nq > Nk,  */
+                             /* or a tensor above 2^31 elements                  */
+    FA_ERR_DTYPE = 3,        /* dtype / grad_dtype not one of fa_dtype_t         */
+    FA_ERR_UNSUPPORTED = 4,  /* head dimension d other than 64 or 128           */
+    FA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the query says    */
+    FA_ERR_HIP = 6,          /* the HIP runtime refused a launch                 */
+    FA_ERR_ARG = 7           /* scale not finite or not > 0                       */
+} fa_status_t;
+
+typedef enum {
+    FA_F32 = 0,
+    FA_BF16 = 1
+} fa_dtype_t;
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/*
+ * Forward pass.
+ *   q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] in dtype; o [B,Hq,Nq,d] in dtype (written);
+ *   lse [B,Hq,Nq] float32 (written; needed by fa_bwd).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   fa_dtype_t dtype, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: one float32 per query row
+ * (D_i = dO_i . O_i), i.e. linear in Nq, never Nq x Nk. */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
+
+/*
+ * Backward pass: gradients of sum(O * dO) with respect to q, k, v.
+ *   q, k, v, o (the forward output), dO in dtype, lse from fa_fwd;
+ *   dq [B,Hq,Nq,d], dk/dv [B,Hkv,Nk,d] written in grad_dtype (FA_F32 is the
+ *   default choice; FA_BF16 rounds the float32 result to bfloat16).  With
+ *   grouped heads, dk/dv of a K/V head are the sums over its query heads.
+ *   The result is deterministic (no atomics): repeated calls give the same bits.
+ *   workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, fa_dtype_t grad_dtype,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   fa_dtype_t dtype, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fa_decode needs for its per-split partial results
+ * (float32 partial outputs and logsumexps), linear in Nmax. */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d);
+
+/*
+ * Decode: one new query token per (b, h) against a KV cache.
+ *   q [B,Hq,1,d]; k_cache/v_cache [B,Hkv,Nmax,d]; seqlens [B] int32 on the
+ *   DEVICE: row b sees keys j < seqlens[b] (values are clamped to [0, Nmax];
+ *   the cache beyond seqlens[b] is never read into the result and may hold
+ *   anything, NaN included).  o [B,Hq,1,d] in dtype; lse [B,Hq] float32.
+ *   seqlens[b] == 0 gives o = 0 and lse = -inf for that sequence.
+ *   workspace: device buffer of at least fa_decode_workspace_bytes(...) bytes.
+ */
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seqlens, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nmax, int d,
+                      fa_dtype_t dtype, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

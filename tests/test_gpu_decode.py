@@ -1,0 +1,83 @@
+"""fa_decode on the GPU against the fp64 oracle: the full GQA decode
+configuration, ragged cache lengths, group sizes, and a poisoned cache tail."""
+import numpy as np
+import pytest
+
+import exact_io_aware_16_amd as fa
+import oracle
+import workloads as W
+from gpu_helpers import TOL_BF16, TOL_F32, announce, assert_close, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(q, k, v, lens, scale):
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    ld = to_device(np.asarray(lens, dtype=np.int32))
+    o, lse = fa.decode(qd, kd, vd, ld, scale=scale)
+    return to_host(o), to_host(lse)
+
+
+def test_config4_gqa_decode_full():
+    w = W.make_config(4)
+    announce(f"config 4: decode B16 Hq32 Hkv8 Nmax32768 d128, lengths {w.seqlens.tolist()}")
+    o, lse = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], w.seqlens, w.scale)
+    O, L = oracle.ref_decode(w.values("q"), w.values("k"), w.values("v"), w.seqlens, scale=w.scale)
+    assert_close("O", o, O, TOL_BF16)
+    assert_close("LSE", lse, L, TOL_BF16)
+
+
+CASES = [
+    # (B, Hq, Hkv, Nmax, d, lengths)
+    (4, 4, 1, 1024, 128, [1, 127, 128, 129]),
+    (4, 8, 2, 2048, 64, [511, 512, 513, 2048]),
+    (3, 32, 8, 4096, 128, [4096, 1000, 2]),
+    (2, 32, 1, 700, 128, [700, 333]),          # MQA, 32 heads in one tile
+    (2, 64, 1, 600, 64, [600, 5]),             # 64 heads per group: two head tiles
+    (2, 6, 6, 1500, 128, [1500, 1499]),        # g = 1
+    (3, 4, 2, 900, 128, [0, 900, 17]),         # empty sequence -> O = 0, LSE = -inf
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}")
+def test_decode_shapes(case, dtype):
+    B, Hq, Hkv, Nmax, d, lens = case
+    w = W.random_case(Nmax + Hq, B, Hq, Hkv, 1, Nmax, d, dtype=dtype)
+    announce(f"decode {case} {dtype}")
+    o, lse = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], lens, w.scale)
+    O, L = oracle.ref_decode(w.values("q"), w.values("k"), w.values("v"), np.array(lens), scale=w.scale)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert_close("O", o, O, tol)
+    assert_close("LSE", lse, L, tol)
+
+
+def test_poisoned_tail_is_never_read_into_the_result():
+    B, Hq, Hkv, Nmax, d = 3, 8, 2, 2000, 128
+    lens = np.array([1500, 1, 777], dtype=np.int32)
+    w = W.random_case(11, B, Hq, Hkv, 1, Nmax, d)
+    k, v = w.tensors["k"].copy(), w.tensors["v"].copy()
+    o1, l1 = run_decode(w.tensors["q"], k, v, lens, w.scale)
+    for b in range(B):
+        k[b, :, lens[b]:] = 0x7FC0   # NaN
+        v[b, :, lens[b]:] = 0x7F80   # +inf
+    o2, l2 = run_decode(w.tensors["q"], k, v, lens, w.scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.isfinite(o2).all()
+
+
+def test_decode_is_deterministic():
+    w = W.make_config(4, B=4, Nk=8192)
+    o1, l1 = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], w.seqlens, w.scale)
+    o2, l2 = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], w.seqlens, w.scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_equals_forward_with_one_query():
+    w = W.random_case(5, 2, 8, 2, 1, 640, 128)
+    lens = np.array([640, 640], dtype=np.int32)
+    o_dec, l_dec = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], lens, w.scale)
+    q, k, v = (to_device(w.tensors[n]) for n in ("q", "k", "v"))
+    o_f, l_f = fa.fwd(q, k, v, causal=False, scale=w.scale)
+    assert np.abs(o_dec - to_host(o_f)).max() <= 2e-2
+    assert np.abs(l_dec - to_host(l_f)[:, :, 0]).max() <= 2e-2
