@@ -113,7 +113,7 @@ struct DqTile {
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
     static constexpr int KIT = (BN / 4) * (D / 8);     // 4-row items for K (threads 0..KIT-1)
     static constexpr int VCH = BN * D / 8;             // 16-byte chunks of V
-    static constexpr int VPT = VCH / (256 - KIT);      // per thread for threads KIT..255
+    static constexpr int VPT = (VCH + 255 - KIT) / (256 - KIT);  // per thread for threads KIT..255
 };
 
 template <int D, bool CAUSAL, typename G>
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         } else {
 #pragma unroll
             for (int r = 0; r < T::VPT; ++r) {
-                const int c = (tid - T::KIT) + (256 - T::KIT) * r;
+                const int c = min((tid - T::KIT) + (256 - T::KIT) * r, T::VCH - 1);
                 const int row = c / (D / 8), c8 = c % (D / 8);
                 const int key = min(key0 + row, kv_end - 1);
                 vr[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c8 * 8);
@@ -182,8 +182,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
             for (int r = 0; r < T::VPT; ++r) {
                 const int c = (tid - T::KIT) + (256 - T::KIT) * r;
-                const int row = c / (D / 8), c8 = c % (D / 8);
-                *reinterpret_cast<u32x4*>(sV + row * T::KS + c8 * 8) = vr[r];
+                if (c < T::VCH) {
+                    const int row = c / (D / 8), c8 = c % (D / 8);
+                    *reinterpret_cast<u32x4*>(sV + row * T::KS + c8 * 8) = vr[r];
+                }
             }
         }
     };
@@ -309,8 +311,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             const int kq = t / (D / 8), c8 = t % (D / 8);
             load4<D>(rr, (tid < T::IT ? Q : dO) + base * D, q0 + kq * 4, Nq, c8);
         }
-        const int lt = tid - 2 * T::IT;
-        if (lt >= 0 && lt < 2 * T::BQ) {
+        const int lt = tid;   // threads 0 .. 2*BQ-1 also fetch lse2 (first BQ) and delta (next BQ)
+        if (lt < 2 * T::BQ) {
             const int qrow = min(q0 + (lt % T::BQ), Nq - 1);
             if (lt < T::BQ) {
                 const float l = LSE[base + qrow];
@@ -328,8 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             uint16_t* tr = st + 2 * T::NAT + (tid < T::IT ? 0 : T::TR);
             store4<T::RS, T::TS>(rr, nat, tr, kq * 4, c8);
         }
-        const int lt = tid - 2 * T::IT;
-        if (lt >= 0 && lt < 2 * T::BQ) reinterpret_cast<float*>(st + 2 * T::NAT + 2 * T::TR)[lt] = aux;
+        if (tid < 2 * T::BQ) reinterpret_cast<float*>(st + 2 * T::NAT + 2 * T::TR)[tid] = aux;
     };
 
     if (total > 0) {
@@ -440,12 +441,15 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict
     const int qi = blockIdx.x * 64 + row;
     const int off = Nk - Nq;
     const size_t qr = (size_t)(b * Hq + h) * Nq + min(qi, Nq - 1);
-    float q[DS], d_o[DS], dq[DS];
+    // gradient sums run over up to g * N terms: accumulated in float64 so the
+    // float32 path stays within a few ulps of the exact result
+    float q[DS], d_o[DS];
+    double dq[DS];
 #pragma unroll
     for (int c = 0; c < DS; ++c) {
         q[c] = Q[qr * D + part * DS + c];
         d_o[c] = dO[qr * D + part * DS + c];
-        dq[c] = 0.f;
+        dq[c] = 0.0;
     }
     const float l = LSE[qr];
     const float lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
@@ -479,12 +483,12 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict
             const float p = ok ? exp2_fast(__builtin_fmaf(s, sl2, -lse2)) : 0.f;
             const float ds = p * (dp - dl);
 #pragma unroll
-            for (int c = 0; c < DS; ++c) dq[c] = __builtin_fmaf(ds, sK[j][part * DS + c], dq[c]);
+            for (int c = 0; c < DS; ++c) dq[c] = __builtin_fma((double)ds, (double)sK[j][part * DS + c], dq[c]);
         }
     }
     if (qi < Nq) {
 #pragma unroll
-        for (int c = 0; c < DS; ++c) dQ[qr * D + part * DS + c] = dq[c] * scale;
+        for (int c = 0; c < DS; ++c) dQ[qr * D + part * DS + c] = (float)(dq[c] * scale);
     }
 }
 
@@ -504,13 +508,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
     const int kj = blockIdx.x * 64 + row;
     const int off = Nk - Nq;
     const size_t kr = (size_t)(b * Hkv + hk) * Nk + min(kj, Nk - 1);
-    float k[DS], v[DS], dk[DS], dv[DS];
+    float k[DS], v[DS];
+    double dk[DS], dv[DS];   // float64 sums over g * N query rows
 #pragma unroll
     for (int c = 0; c < DS; ++c) {
         k[c] = K[kr * D + part * DS + c];
         v[c] = V[kr * D + part * DS + c];
-        dk[c] = 0.f;
-        dv[c] = 0.f;
+        dk[c] = 0.0;
+        dv[c] = 0.0;
     }
     const int q_begin = causal ? max(0, (int)blockIdx.x * 64 - off) : 0;
     for (int hq = hk * g; hq < hk * g + g; ++hq) {
@@ -547,8 +552,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
                 const float ds = p * (dp - sD[i]);
 #pragma unroll
                 for (int c = 0; c < DS; ++c) {
-                    dv[c] = __builtin_fmaf(p, sdO[i][part * DS + c], dv[c]);
-                    dk[c] = __builtin_fmaf(ds, sQ[i][part * DS + c], dk[c]);
+                    dv[c] = __builtin_fma((double)p, (double)sdO[i][part * DS + c], dv[c]);
+                    dk[c] = __builtin_fma((double)ds, (double)sQ[i][part * DS + c], dk[c]);
                 }
             }
         }
@@ -556,8 +561,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
     if (kj < Nk) {
 #pragma unroll
         for (int c = 0; c < DS; ++c) {
-            dK[kr * D + part * DS + c] = dk[c] * scale;
-            dV[kr * D + part * DS + c] = dv[c];
+            dK[kr * D + part * DS + c] = (float)(dk[c] * scale);
+            dV[kr * D + part * DS + c] = (float)dv[c];
         }
     }
 }

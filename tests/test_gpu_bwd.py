@@ -1,0 +1,94 @@
+"""fa_bwd on the GPU against the fp64 oracle gradients.
+
+The GPU backward consumes what fa_fwd produced (O in the input dtype and the
+float32 row logsumexp), as a training step would; the oracle differentiates the
+exact definition.  Tolerances: bf16 inputs max-abs 2e-2 and rel-L2 5e-3 on dQ,
+dK, dV (float32 gradients); fp32 inputs max-abs 1e-5."""
+import numpy as np
+import pytest
+
+import exact_io_aware_16_amd as fa
+import oracle
+import workloads as W
+from gpu_helpers import TOL_BF16, TOL_F32, announce, assert_close, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(w, causal, grad_dtype=None):
+    import torch
+    q, k, v, do = (to_device(w.tensors[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=w.scale, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return to_host(o), to_host(lse), to_host(dq), to_host(dk), to_host(dv)
+
+
+def test_config5_fwd_bwd_full():
+    w = W.make_config(5)
+    announce("config 5: B2 H16 N4096 d128 bf16 causal fwd+bwd (full fp64 oracle)")
+    o, lse, dq, dk, dv = run_fwd_bwd(w, True)
+    q, k, v, do = (w.values(n) for n in ("q", "k", "v", "do"))
+    O, L = oracle.ref_fwd(q, k, v, causal=True, scale=w.scale)
+    assert_close("O", o, O, TOL_BF16)
+    assert_close("LSE", lse, L, TOL_BF16)
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, causal=True, scale=w.scale)
+    assert_close("dQ", dq, dQ, TOL_BF16)
+    assert_close("dK", dk, dK, TOL_BF16)
+    assert_close("dV", dv, dV, TOL_BF16)
+
+
+SHAPES = [
+    # (B, Hq, Hkv, Nq, Nk, d, causal)
+    (1, 1, 1, 1, 1, 64, True),
+    (1, 2, 2, 63, 63, 128, True),
+    (2, 2, 1, 65, 65, 64, False),
+    (1, 4, 2, 257, 257, 128, True),       # GQA g=2, ragged
+    (1, 8, 1, 300, 300, 64, True),        # MQA g=8
+    (1, 4, 4, 100, 90, 128, False),       # Nq != Nk
+    (1, 2, 2, 77, 333, 64, True),         # bottom-right causal
+    (2, 4, 1, 1000, 1000, 128, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}x{}N{}x{}d{}{}".format(*s[:6], "c" if s[6] else ""))
+def test_bwd_edge_shapes(shape, dtype):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    w = W.random_case(sum(shape[:6]) + 3, B, Hq, Hkv, Nq, Nk, d, dtype=dtype, with_do=True)
+    announce(f"bwd edge {shape} {dtype}")
+    o, lse, dq, dk, dv = run_fwd_bwd(w, causal)
+    q, k, v, do = (w.values(n) for n in ("q", "k", "v", "do"))
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, causal=causal, scale=w.scale)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert_close("dQ", dq, dQ, tol)
+    assert_close("dK", dk, dK, tol)
+    assert_close("dV", dv, dV, tol)
+
+
+def test_bf16_gradients():
+    """grad_dtype bf16: the float32 result rounded to bf16 (same tolerance)."""
+    import torch
+    w = W.random_case(41, 1, 4, 2, 512, 512, 128, with_do=True)
+    _, _, dq, dk, dv = run_fwd_bwd(w, True, grad_dtype=torch.bfloat16)
+    q, k, v, do = (w.values(n) for n in ("q", "k", "v", "do"))
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, causal=True, scale=w.scale)
+    assert_close("dQ(bf16)", dq, dQ, TOL_BF16)
+    assert_close("dK(bf16)", dk, dK, TOL_BF16)
+    assert_close("dV(bf16)", dv, dV, TOL_BF16)
+
+
+def test_bwd_is_deterministic():
+    w = W.random_case(43, 2, 8, 2, 700, 700, 128, with_do=True)
+    a = run_fwd_bwd(w, True)
+    b = run_fwd_bwd(w, True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_gradient_identities_on_gpu():
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i (MHA), within bf16 tolerance."""
+    w = W.random_case(47, 1, 2, 2, 384, 384, 64, with_do=True)
+    _, _, dq, dk, dv = run_fwd_bwd(w, True)
+    assert np.abs(dk.sum(axis=2)).max() <= 2e-2 * np.sqrt(384)
+    assert np.abs(dv.sum(axis=2) - w.values("do").astype(np.float64).sum(axis=2)).max() <= 2e-2 * np.sqrt(384)
