@@ -49,6 +49,8 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
+    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode"], default=None,
+                    help="run only this row (for profiling one kernel); prints the row as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain 256 MiB device copies (known bytes) to scale rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counts")
@@ -285,6 +287,11 @@ def main():
     import exact_io_aware_16_amd as fa
     import workloads as W
     fa.load_library()   # raises if libfa.so is not built: there is no other path
+
+    if args.only:
+        fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode}[args.only]
+        print(json.dumps({args.only: fn(args, fa, W)}), flush=True)
+        return
 
     log("headline: causal forward B4 H16 N2048 d64 bf16")
     head = headline(args, fa, W)

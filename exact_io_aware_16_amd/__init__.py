@@ -33,6 +33,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_16_amd.build`")
+    # torch ships its own HIP runtime and requests it as "libamdhip64.so";
+    # libfa requests "libamdhip64.so.7".  Loading torch first lets libfa's
+    # request resolve (by SONAME) to torch's copy, so one runtime serves both
+    # and torch's stream handles are valid in libfa.  The other order would
+    # map two runtimes into the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_abi_version.restype = i

@@ -31,39 +31,13 @@ namespace fa {
 
 namespace {
 
-// Same permutation as the forward pass: key kappa of a 32-key group lands at
-// the slot where a lane half finds its eight keys contiguously, in the order
-// its score registers hold them.
-__device__ __forceinline__ int perm32(int kappa) {
-    const int mt = kappa >> 5, g = (kappa >> 3) & 3, hh = (kappa >> 2) & 1;
-    return mt * 32 + (g >> 1) * 16 + hh * 8 + (g & 1) * 4;
-}
-
-// Loads four consecutive rows (clamped to row_end - 1) of an 8-column chunk.
+// Row strides of the LDS tiles: RS for 16-byte row reads (each 16-lane group
+// hits 16 distinct bank quads), TS (64 B mod 256 B) for the transposing reads.
 template <int D>
-__device__ __forceinline__ void load4(u32x4 (&r)[4], const uint16_t* __restrict__ base, int row0, int row_end,
-                                      int c8) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = min(row0 + u, row_end - 1);
-        r[u] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + c8 * 8);
-    }
-}
-
-// Writes four rows as is (stride S) and transposed (stride TS, permuted slot).
-template <int S, int TS>
-__device__ __forceinline__ void store4(const u32x4 (&r)[4], uint16_t* nat, uint16_t* tr, int row0, int c8) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(nat + (row0 + u) * S + c8 * 8) = r[u];
-    if (tr) {
-        const int pos = perm32(row0);
-        static_for<0, 8>([&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            *reinterpret_cast<u32x2*>(tr + (c8 * 8 + e) * TS + pos) =
-                u32x2{pack_col<e>(r[0], r[1]), pack_col<e>(r[2], r[3])};
-        });
-    }
-}
+struct Strides {
+    static constexpr int RS = D + 8;
+    static constexpr int TS = D + 32;
+};
 
 __device__ __forceinline__ void store_grad4(float* dst, float a, float b, float c, float d) {
     *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
@@ -106,14 +80,11 @@ template <int D>
 struct DqTile {
     static constexpr int BM = 128;       // queries per workgroup (4 waves x 32)
     static constexpr int BN = 32;        // keys per block
-    static constexpr int KS = D + 8;     // K / V row stride
-    static constexpr int TS = BN + 8;    // K^T row stride
-    static constexpr int K_EL = BN * KS, KT_EL = D * TS, V_EL = BN * KS;
+    static constexpr int RS = Strides<D>::RS, TS = Strides<D>::TS;
+    static constexpr int K_EL = BN * RS, KT_EL = BN * TS, V_EL = BN * RS;
     static constexpr int STAGE = K_EL + KT_EL + V_EL;
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int KIT = (BN / 4) * (D / 8);     // 4-row items for K (threads 0..KIT-1)
-    static constexpr int VCH = BN * D / 8;             // 16-byte chunks of V
-    static constexpr int VPT = (VCH + 255 - KIT) / (256 - KIT);  // per thread for threads KIT..255
+    static constexpr int CPT = BN * D / 8 / 256;   // 16-byte chunks per thread per tensor
 };
 
 template <int D, bool CAUSAL, typename G>
@@ -158,35 +129,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) acc[md] = zero16();
 
-    u32x4 kr[4], vr[T::VPT];
+    // K is staged twice (row-read stride for S^T = K Q^T, transpose-read stride
+    // for dQ^T = K^T dS^T); V once.  Rows at or past kv_end read row kv_end - 1.
+    u32x4 kr[T::CPT], vr[T::CPT];
     auto load = [&](int key0) {
-        if (tid < T::KIT) {
-            const int kq = tid / (D / 8), c8 = tid % (D / 8);
-            load4<D>(kr, kb, key0 + kq * 4, kv_end, c8);
-        } else {
 #pragma unroll
-            for (int r = 0; r < T::VPT; ++r) {
-                const int c = min((tid - T::KIT) + (256 - T::KIT) * r, T::VCH - 1);
-                const int row = c / (D / 8), c8 = c % (D / 8);
-                const int key = min(key0 + row, kv_end - 1);
-                vr[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c8 * 8);
-            }
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), c8 = c % (D / 8);
+            const size_t gi = (size_t)min(key0 + row, kv_end - 1) * D + c8 * 8;
+            kr[r] = *reinterpret_cast<const u32x4*>(kb + gi);
+            vr[r] = *reinterpret_cast<const u32x4*>(vb + gi);
         }
     };
     auto store = [&](uint16_t* st) {
-        if (tid < T::KIT) {
-            const int kq = tid / (D / 8), c8 = tid % (D / 8);
-            store4<T::KS, T::TS>(kr, st, st + T::K_EL, kq * 4, c8);
-        } else {
-            uint16_t* sV = st + T::K_EL + T::KT_EL;
 #pragma unroll
-            for (int r = 0; r < T::VPT; ++r) {
-                const int c = (tid - T::KIT) + (256 - T::KIT) * r;
-                if (c < T::VCH) {
-                    const int row = c / (D / 8), c8 = c % (D / 8);
-                    *reinterpret_cast<u32x4*>(sV + row * T::KS + c8 * 8) = vr[r];
-                }
-            }
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), c8 = c % (D / 8);
+            *reinterpret_cast<u32x4*>(st + row * T::RS + c8 * 8) = kr[r];
+            *reinterpret_cast<u32x4*>(st + T::K_EL + row * T::TS + c8 * 8) = kr[r];
+            *reinterpret_cast<u32x4*>(st + T::K_EL + T::KT_EL + row * T::RS + c8 * 8) = vr[r];
         }
     };
 
@@ -204,8 +167,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sK + n * T::KS + kk * 16 + hf * 8), qf[kk], s);
-                dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sV + n * T::KS + kk * 16 + hf * 8), df[kk], dp);
+                s = mfma32x32x16(frag_rows(sK, T::RS, 0, kk * 16, lane), qf[kk], s);
+                dp = mfma32x32x16(frag_rows(sV, T::RS, 0, kk * 16, lane), df[kk], dp);
             }
             const bool need_mask = key0 + T::BN > kv_end || (CAUSAL && key0 + T::BN > qw + off);
 #pragma unroll
@@ -225,8 +188,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 for (int e = 0; e < 8; ++e) db[e] = (__bf16)s[ks * 8 + e];
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md)
-                    acc[md] = mfma32x32x16(
-                        *reinterpret_cast<const bf16x8*>(sKT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), db, acc[md]);
+                    acc[md] = mfma32x32x16(frag_tr(sKT, T::TS, ks * 16, md * 32, lane), db, acc[md]);
             }
         }
         if (j + 1 < nblk) store(smem + ((j + 1) & 1) * T::STAGE);
@@ -250,12 +212,11 @@ template <int D>
 struct DkvTile {
     static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
     static constexpr int BQ = 32;        // queries per block
-    static constexpr int RS = D + 8;     // Q / dO row stride
-    static constexpr int TS = BQ + 8;    // Q^T / dO^T row stride
-    static constexpr int NAT = BQ * RS, TR = D * TS;
+    static constexpr int RS = Strides<D>::RS, TS = Strides<D>::TS;
+    static constexpr int NAT = BQ * RS, TR = BQ * TS;
     static constexpr int STAGE = 2 * NAT + 2 * TR + 2 * BQ * 2;  // + lse2 and delta (float = 2 elems)
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int IT = (BQ / 4) * (D / 8);  // 4-row items per tensor
+    static constexpr int CPT = BQ * D / 8 / 256;   // 16-byte chunks per thread per tensor
 };
 
 template <int D, bool CAUSAL, typename G>
@@ -300,35 +261,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int total = g * nqblk;   // (head, query block) steps
     const int wave_q_begin = CAUSAL ? max(0, kw - off) : 0;
 
-    u32x4 rr[4];
+    // Q and dO are each staged twice: row-read stride (S = Q K^T, dP = dO V^T)
+    // and transpose-read stride (dK^T += Q^T dS, dV^T += dO^T P).  Threads
+    // 0 .. 2*BQ-1 also fetch lse*log2(e) (rows past Nq or with no visible key
+    // get +inf, i.e. P = 0) and D.
+    u32x4 qr[T::CPT], dr[T::CPT];
     float aux = 0.f;
     auto load = [&](int step) {
         const int hq = hk * g + step / nqblk;
         const int q0 = (qb0 + step % nqblk) * T::BQ;
         const size_t base = (size_t)(b * Hq + hq) * Nq;
-        if (tid < 2 * T::IT) {
-            const int t = tid % T::IT;
-            const int kq = t / (D / 8), c8 = t % (D / 8);
-            load4<D>(rr, (tid < T::IT ? Q : dO) + base * D, q0 + kq * 4, Nq, c8);
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), c8 = c % (D / 8);
+            const size_t gi = (base + min(q0 + row, Nq - 1)) * D + c8 * 8;
+            qr[r] = *reinterpret_cast<const u32x4*>(Q + gi);
+            dr[r] = *reinterpret_cast<const u32x4*>(dO + gi);
         }
-        const int lt = tid;   // threads 0 .. 2*BQ-1 also fetch lse2 (first BQ) and delta (next BQ)
-        if (lt < 2 * T::BQ) {
-            const int qrow = min(q0 + (lt % T::BQ), Nq - 1);
-            if (lt < T::BQ) {
+        if (tid < 2 * T::BQ) {
+            const int qrow = min(q0 + (tid % T::BQ), Nq - 1);
+            if (tid < T::BQ) {
                 const float l = LSE[base + qrow];
-                aux = (q0 + lt < Nq && l != kNegInf) ? l * kLog2e : __builtin_huge_valf();
+                aux = (q0 + tid < Nq && l != kNegInf) ? l * kLog2e : __builtin_huge_valf();
             } else {
                 aux = delta[base + qrow];
             }
         }
     };
     auto store = [&](uint16_t* st) {
-        if (tid < 2 * T::IT) {
-            const int t = tid % T::IT;
-            const int kq = t / (D / 8), c8 = t % (D / 8);
-            uint16_t* nat = st + (tid < T::IT ? 0 : T::NAT);
-            uint16_t* tr = st + 2 * T::NAT + (tid < T::IT ? 0 : T::TR);
-            store4<T::RS, T::TS>(rr, nat, tr, kq * 4, c8);
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), c8 = c % (D / 8);
+            *reinterpret_cast<u32x4*>(st + row * T::RS + c8 * 8) = qr[r];
+            *reinterpret_cast<u32x4*>(st + T::NAT + row * T::RS + c8 * 8) = dr[r];
+            *reinterpret_cast<u32x4*>(st + 2 * T::NAT + row * T::TS + c8 * 8) = qr[r];
+            *reinterpret_cast<u32x4*>(st + 2 * T::NAT + T::TR + row * T::TS + c8 * 8) = dr[r];
         }
         if (tid < 2 * T::BQ) reinterpret_cast<float*>(st + 2 * T::NAT + 2 * T::TR)[tid] = aux;
     };
@@ -352,8 +321,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sQ + n * T::RS + kk * 16 + hf * 8), kf[kk], s);
-                dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sdO + n * T::RS + kk * 16 + hf * 8), vf[kk], dp);
+                s = mfma32x32x16(frag_rows(sQ, T::RS, 0, kk * 16, lane), kf[kk], s);
+                dp = mfma32x32x16(frag_rows(sdO, T::RS, 0, kk * 16, lane), vf[kk], dp);
             }
             const bool need_mask = kw + 32 > Nk || (CAUSAL && kw + 31 > q0 + off);
 #pragma unroll
@@ -383,10 +352,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                 }
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md) {
-                    dv[md] = mfma32x32x16(
-                        *reinterpret_cast<const bf16x8*>(sdOT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), pb, dv[md]);
-                    dk[md] = mfma32x32x16(
-                        *reinterpret_cast<const bf16x8*>(sQT + (md * 32 + n) * T::TS + ks * 16 + hf * 8), db, dk[md]);
+                    dv[md] = mfma32x32x16(frag_tr(sdOT, T::TS, ks * 16, md * 32, lane), pb, dv[md]);
+                    dk[md] = mfma32x32x16(frag_tr(sQT, T::TS, ks * 16, md * 32, lane), db, dk[md]);
                 }
             }
         }

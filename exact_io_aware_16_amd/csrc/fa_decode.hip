@@ -30,20 +30,15 @@ constexpr int DBN = 128;  // keys per sub-block (4 waves x 32)
 
 template <int D>
 struct DecTile {
-    static constexpr int KS = D + 8;
-    static constexpr int VS = DBN + 8;
+    static constexpr int KS = D + 8;    // K row stride (row reads: distinct bank quads)
+    static constexpr int VS = D + 32;   // V row stride (64 B mod 256 B: transpose reads 2-way)
     static constexpr int K_ELEMS = DBN * KS;
-    static constexpr int V_ELEMS = D * VS;
+    static constexpr int V_ELEMS = DBN * VS;
     static constexpr int LDS_BYTES = (K_ELEMS + V_ELEMS) * 2;
-    static constexpr int KPT = DBN * D / 8 / 256;        // 16-byte K chunks per thread
-    static constexpr int VPT = (DBN / 4) * (D / 8) / 256;  // (4-key, 8-col) V items per thread
+    static constexpr int CPT = DBN * D / 8 / 256;   // 16-byte chunks per thread per tensor
 };
 
-__device__ __forceinline__ int vt_pos32(int kappa) {
-    // permutation inside each group of 32 keys; see the forward kernel
-    const int mt = kappa >> 5, g = (kappa >> 3) & 3, hh = (kappa >> 2) & 1;
-    return mt * 32 + (g >> 1) * 16 + hh * 8 + (g & 1) * 4;
-}
+constexpr float kRescaleThreshold = 8.0f;   // lazy rescaling, as in the forward kernel
 
 }  // namespace
 
@@ -88,44 +83,26 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     // Keys at or past k_end are read from row k_end - 1 (a valid, finite row of
     // this sequence): their scores are masked to -inf so they carry weight
     // exactly 0, and the cache beyond the sequence length is never touched.
-    u32x4 kr[T::KPT], vr[T::VPT][4];
+    // 16 consecutive threads move one 256-byte key row (full-row loads, one
+    // contiguous LDS run per row).
+    u32x4 kr[T::CPT], vr[T::CPT];
     auto load = [&](int key0) {
 #pragma unroll
-        for (int r = 0; r < T::KPT; ++r) {
+        for (int r = 0; r < T::CPT; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 8), col8 = c % (D / 8);
-            const int key = min(key0 + row, k_end - 1);
-            kr[r] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + col8 * 8);
-        }
-#pragma unroll
-        for (int r = 0; r < T::VPT; ++r) {
-            const int it = tid + 256 * r;
-            const int kq = it / (D / 8), c8 = it % (D / 8);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int key = min(key0 + kq * 4 + u, k_end - 1);
-                vr[r][u] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c8 * 8);
-            }
+            const size_t gi = (size_t)min(key0 + row, k_end - 1) * D + col8 * 8;
+            kr[r] = *reinterpret_cast<const u32x4*>(kb + gi);
+            vr[r] = *reinterpret_cast<const u32x4*>(vb + gi);
         }
     };
     auto store = [&]() {
 #pragma unroll
-        for (int r = 0; r < T::KPT; ++r) {
+        for (int r = 0; r < T::CPT; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 8), col8 = c % (D / 8);
             *reinterpret_cast<u32x4*>(sK + row * T::KS + col8 * 8) = kr[r];
-        }
-#pragma unroll
-        for (int r = 0; r < T::VPT; ++r) {
-            const int it = tid + 256 * r;
-            const int kq = it / (D / 8), c8 = it % (D / 8);
-            const int pos = vt_pos32(kq * 4);
-            static_for<0, 8>([&](auto ec) {
-                constexpr int e = decltype(ec)::value;
-                const uint32_t lo = pack_col<e>(vr[r][0], vr[r][1]);
-                const uint32_t hi = pack_col<e>(vr[r][2], vr[r][3]);
-                *reinterpret_cast<u32x2*>(sV + (c8 * 8 + e) * T::VS + pos) = u32x2{lo, hi};
-            });
+            *reinterpret_cast<u32x4*>(sV + row * T::VS + col8 * 8) = vr[r];
         }
     };
 
@@ -143,10 +120,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
         const int wkey0 = key0 + wave * 32;
         if (wkey0 < k_end) {
             f32x16 sc = zero16();
-            const uint16_t* ka = sK + (wave * 32 + n) * T::KS + hf * 8;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
-                sc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ka + kk * 16), qf[kk], sc);
+                sc = mfma32x32x16(frag_rows(sK, T::KS, wave * 32, kk * 16, lane), qf[kk], sc);
             if (wkey0 + 32 > k_end) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -157,18 +133,18 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
             float mx = kNegInf;
 #pragma unroll
             for (int i = 0; i < 16; i += 2) mx = max3f(mx, sc[i], sc[i + 1]);
-            mx = __builtin_fmaxf(mx, xor32(mx));
-            const float m_new = __builtin_fmaxf(m_run, mx * sl2);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            if (!wave_all(m_new == m_run)) {
-                const float corr = exp2_fast(m_run - m_use);
+            mx = pair_max(mx) * sl2;
+            if (!wave_all(mx <= m_run + kRescaleThreshold)) {
+                const float m_new = __builtin_fmaxf(m_run, mx);
+                const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
                 l_run *= corr;
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) ot[md][i] *= corr;
+                m_run = m_new;
             }
-            m_run = m_new;
+            const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -m_use));
@@ -180,10 +156,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
                 bf16x8 pb;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[ks * 8 + e];
-                const uint16_t* va = sV + n * T::VS + wave * 32 + ks * 16 + hf * 8;
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md)
-                    ot[md] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(va + md * 32 * T::VS), pb, ot[md]);
+                    ot[md] = mfma32x32x16(frag_tr(sV, T::VS, wave * 32 + ks * 16, md * 32, lane), pb, ot[md]);
             }
         }
         __syncthreads();
@@ -193,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     float* sm = reinterpret_cast<float*>(smem);   // [4][32] max
     float* sl = sm + 128;                         // [4][32] sum
     float* so = sl + 128;                         // [4][32][D] scaled outputs
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     if (hf == 0) {
         sm[wave * 32 + n] = m_run;
         sl[wave * 32 + n] = l_tot;

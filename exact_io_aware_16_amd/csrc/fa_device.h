@@ -31,6 +31,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// (1.0, 1.0) in bf16, the second operand of row sums done with v_dot2c_f32_bf16.
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,8 +66,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-// Value of lane (l ^ 32) for every lane l.
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// max / sum of x over the lane pair (l, l ^ 32), on v_permlane32_swap: the
+// swap hands each lane both halves' values without going through LDS.
+__device__ __forceinline__ float pair_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
@@ -73,6 +85,36 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 
 // Wave-uniform "all lanes true".
 __device__ __forceinline__ bool wave_all(bool p) { return __all(p); }
+
+// ---------------------------------------------------------------------------
+// Matrix-core operand fragments read from LDS tiles stored row-major
+// (row = key or query, d contiguous).
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// A (or B) fragment of X itself: lane l gets X[r0 + l%32][c0 + 8*(l/32) .. +7]
+// (one 16-byte read).
+__device__ __forceinline__ bf16x8 frag_rows(const uint16_t* X, int S, int r0, int c0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(X + (r0 + (lane & 31)) * S + c0 + (lane >> 5) * 8);
+}
+
+// A fragment of X^T (rows of the fragment = columns of X, k = rows of X) from
+// the same row-major tile, with two ds_read_b64_tr_b16: lane l gets
+// X[k0 + 8*(e/4) + 4*(l/32) + e%4][c0 + l%32] for e = 0..7.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
+// 8-byte chunks addressed by lanes 4j + i/4 (j = 0..3), i.e. it transposes a
+// 4-row x 16-column block; each lane therefore addresses row k0 + 4*(l/32) +
+// (l%16)/4 at column c0 + 16*((l/16)%2) + 4*(l%4).
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* X, int S, int k0, int c0, int lane) {
+    const int t = lane & 15;
+    const int row = k0 + (lane >> 5) * 4 + (t >> 2);
+    const int col = c0 + ((lane >> 4) & 1) * 16 + (t & 3) * 4;
+    const uint16_t* p = X + row * S + col;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * S));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>

@@ -29,99 +29,55 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// Query column tiles per wave for each head dimension.
+#ifndef FWD_NT64
+#define FWD_NT64 1
+#endif
+#ifndef FWD_NT128
+#define FWD_NT128 1
+#endif
+// Causal: pair query blocks (p, nqb-1-p) in one workgroup (1) or issue single
+// blocks heaviest first (0).
+#ifndef FWD_PAIR
+#define FWD_PAIR 0
+#endif
+// Row sums with v_dot2c_f32_bf16 on the packed bf16 P (1) or float adds (0).
+#ifndef FWD_DOT2
+#define FWD_DOT2 0
+#endif
+
 namespace fa {
 
-template <int D>
+template <int D, int NT>
 struct FwdTile {
-    static constexpr int NW = 4;             // waves per workgroup
-    static constexpr int BM = 32 * NW;       // query rows per workgroup
-    static constexpr int BN = 64;            // keys per K/V block
-    static constexpr int KS = D + 8;         // K tile row stride (elements), breaks bank aliasing
-    static constexpr int VS = BN + 8;        // V^T tile row stride (elements)
+    static constexpr int NW = 4;               // waves per workgroup
+    static constexpr int QW = 32 * NT;         // query rows per wave (NT column tiles of 32)
+    static constexpr int BM = NW * QW;         // query rows per workgroup
+    static constexpr int BN = 64;              // keys per K/V block
+    static constexpr int KS = D + 8;           // K row stride: 16-lane row reads hit 16 distinct bank quads
+    static constexpr int VS = D + 32;          // V row stride (64 B mod 256 B): transpose reads 2-way at most
     static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = D * VS;
+    static constexpr int V_ELEMS = BN * VS;
     static constexpr int STAGE = K_ELEMS + V_ELEMS;
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int KCH = BN * D / 8;   // 16-byte chunks in a K block
-    static constexpr int KPT = KCH / 256;    // chunks per thread
-    static constexpr int VIT = (BN / 4) * (D / 8);  // (4-key group, 8-column chunk) items
+    static constexpr int CH = BN * D / 8;      // 16-byte chunks per K (or V) block
+    static constexpr int CPT = CH / 256;       // chunks per thread
 };
 
-// Position of key kappa (0..63, a multiple of 4) inside a transposed V row:
-// kappa = 32*mt + 8*g + 4*hh + r  ->  32*mt + 16*(g/2) + 8*hh + 4*(g%2) + r.
-// Lane half hh then finds the eight keys it multiplies, in the order its P
-// registers hold them, at one contiguous 16-byte slot.
-__device__ __forceinline__ int vt_pos(int kappa) {
-    const int mt = kappa >> 5, g = (kappa >> 3) & 3, hh = (kappa >> 2) & 1;
-    return mt * 32 + (g >> 1) * 16 + hh * 8 + (g & 1) * 4;
-}
+// Lazy rescaling threshold (log2 units): the running max is only raised when
+// some row's block max exceeds it by more than 2^8; until then probabilities
+// up to 2^8 are accumulated against the stale max.  O and l share that max, so
+// the final O / l is unchanged (exact up to rounding).
+constexpr float kRescaleThreshold = 8.0f;
 
-template <int D>
-struct KVStage {
-    u32x4 k[FwdTile<D>::KPT];
-    u32x4 v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_kv_block(KVStage<D>& st, const uint16_t* __restrict__ kb,
-                                              const uint16_t* __restrict__ vb, int key0, int kv_end,
-                                              int tid) {
-    // Rows at or past kv_end are read from row kv_end - 1 instead: always in
-    // bounds and finite; their scores are masked to -inf, so they enter the
-    // result with probability exactly 0.
-    using T = FwdTile<D>;
-#pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int c = tid + 256 * r;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        const int key = min(key0 + row, kv_end - 1);
-        st.k[r] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + col8 * 8);
-    }
-    if (tid < T::VIT) {
-        const int kq = tid / (D / 8), c8 = tid % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = min(key0 + kq * 4 + r, kv_end - 1);
-            st.v[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c8 * 8);
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_kv_block(const KVStage<D>& st, uint16_t* sK, uint16_t* sV, int tid) {
-    using T = FwdTile<D>;
-#pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int c = tid + 256 * r;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(sK + row * T::KS + col8 * 8) = st.k[r];
-    }
-    if (tid < T::VIT) {
-        const int kq = tid / (D / 8), c8 = tid % (D / 8);
-        const int pos = vt_pos(kq * 4);
-        static_for<0, 8>([&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            const uint32_t lo = pack_col<e>(st.v[0], st.v[1]);
-            const uint32_t hi = pack_col<e>(st.v[2], st.v[3]);
-            *reinterpret_cast<u32x2*>(sV + (c8 * 8 + e) * T::VS + pos) = u32x2{lo, hi};
-        });
-    }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
-    float sl2) {
-    using T = FwdTile<D>;
-    extern __shared__ __align__(16) uint16_t smem[];
-
-    const int id = blockIdx.x;
-    const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-    const int bh = id % BH;
-    const int b = bh / Hq, h = bh % Hq;
+// One query block of one (batch, head): the whole online-softmax pass.
+template <int D, int NT, bool CAUSAL>
+__device__ __forceinline__ void fwd_qblock(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                           float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b, int h,
+                                           int qb, float sl2, uint16_t* smem) {
+    using T = FwdTile<D, NT>;
     const int hk = h / (Hq / Hkv);
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, hf = lane >> 5;
@@ -131,134 +87,217 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
 
     const int off = Nk - Nq;  // bottom-right causal alignment
-    const int qw = qb * T::BM + wave * 32;
-    const int qi = qw + n;
+    const int qw = qb * T::BM + wave * T::QW;
 
-    // Q^T as the B operand: lane (n, hf) holds q[qi][16*kk + 8*hf .. +7].
-    bf16x8 qf[D / 16];
-    {
-        // rows past Nq read row Nq - 1; they are computed but never stored
-        const uint16_t* qrow = qbase + (size_t)min(qi, Nq - 1) * D;
+    // Q^T as the B operand: lane (n, hf) of column tile nt holds
+    // q[qw + 32 nt + n][16 kk + 8 hf .. +7]; rows past Nq read row Nq - 1 and are
+    // never stored.
+    bf16x8 qf[NT][D / 16];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* qrow = qbase + (size_t)min(qw + nt * 32 + n, Nq - 1) * D;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-            qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
+            qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
     }
 
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
     const int nblk = (kv_end + T::BN - 1) / T::BN;
-    int wave_end = Nk;  // one past the last key any row of this wave sees
-    if (CAUSAL) wave_end = min(Nk, qw + 32 + off);
-    const int mask_from = CAUSAL ? (qw + off) : Nk;  // first key some row of the wave cannot see
+    const int wave_end = CAUSAL ? min(Nk, qw + T::QW + off) : Nk;  // one past the wave's last visible key
+    const int mask_from = CAUSAL ? (qw + off) : Nk;                 // first key some wave row cannot see
 
-    f32x16 ot[D / 32];
+    f32x16 ot[NT][D / 32];
 #pragma unroll
-    for (int md = 0; md < D / 32; ++md) ot[md] = zero16();
-    float m_run = kNegInf;  // running max of scale*log2(e)*s for query qi
-    float l_run = 0.f;      // running sum over this lane's half of the keys
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md) ot[nt][md] = zero16();
+    float m_run[NT], l_run[NT];   // running max of scale*log2(e)*s; sum over this lane's half of the keys
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+        l_run[nt] = 0.f;
+    }
 
-    KVStage<D> st;
-    load_kv_block<D>(st, kbase, vbase, 0, kv_end, tid);
-    store_kv_block<D>(st, smem, smem + T::K_ELEMS, tid);
+    // K/V staging: thread t moves 16-byte chunks t, t+256, ... of each block;
+    // 16 consecutive threads cover one key row, so every load is a full row
+    // and every LDS store is one contiguous 256-byte run.  Rows at or past
+    // kv_end are read from row kv_end - 1 (in bounds, finite, weight 0).
+    u32x4 kr[T::CPT], vr[T::CPT];
+    auto load = [&](int key0) {
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            const size_t g = (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8;
+            kr[r] = *reinterpret_cast<const u32x4*>(kbase + g);
+            vr[r] = *reinterpret_cast<const u32x4*>(vbase + g);
+        }
+    };
+    auto store = [&](uint16_t* sK) {
+        uint16_t* sV = sK + T::K_ELEMS;
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            *reinterpret_cast<u32x4*>(sK + row * T::KS + col8 * 8) = kr[r];
+            *reinterpret_cast<u32x4*>(sV + row * T::VS + col8 * 8) = vr[r];
+        }
+    };
+
+    load(0);
+    store(smem);
     __syncthreads();
 
     for (int j = 0; j < nblk; ++j) {
         const int key0 = j * T::BN;
-        uint16_t* sK = smem + (j & 1) * T::STAGE;
-        uint16_t* sV = sK + T::K_ELEMS;
-        if (j + 1 < nblk) load_kv_block<D>(st, kbase, vbase, key0 + T::BN, kv_end, tid);
+        const uint16_t* sK = smem + (j & 1) * T::STAGE;
+        const uint16_t* sV = sK + T::K_ELEMS;
+        if (j + 1 < nblk) load(key0 + T::BN);
 
         if (key0 < wave_end) {
-            // ---- S^T = K Q^T for 64 keys x 32 queries --------------------------------
-            f32x16 s[2];
+            // ---- S^T = K Q^T: 64 keys x QW queries -----------------------------------
+            f32x16 s[2][NT];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                s[mt] = zero16();
-                const uint16_t* ka = sK + (mt * 32 + n) * T::KS + hf * 8;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ka + kk * 16);
-                    s[mt] = mfma32x32x16(a, qf[kk], s[mt]);
+                    const bf16x8 a = frag_rows(sK, T::KS, mt * 32, kk * 16, lane);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(a, qf[nt][kk], s[mt][nt]);
                 }
             }
-            // ---- mask (only on blocks that cross the diagonal or the end) ----------
+            // ---- mask (only on blocks that cross the diagonal or the end) --------------
             if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int qi = qw + nt * 32 + n;
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                            const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
+                            s[mt][nt][i] = ok ? s[mt][nt][i] : kNegInf;
+                        }
+                }
+            }
+            // ---- online softmax (base 2, lazy rescale) ----------------------------------
+            float mx[NT];
+            bool grow = false;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float m = kNegInf;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                        const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
-                        s[mt][i] = ok ? s[mt][i] : kNegInf;
-                    }
+                    for (int i = 0; i < 16; i += 2) m = max3f(m, s[mt][nt][i], s[mt][nt][i + 1]);
+                mx[nt] = pair_max(m) * sl2;
+                grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
             }
-            // ---- online softmax (base 2) -------------------------------------------
-            float mx = kNegInf;
+            if (!wave_all(!grow)) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+                for (int nt = 0; nt < NT; ++nt) {
+                    const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
+                    const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
+                    l_run[nt] *= corr;
 #pragma unroll
-                for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[mt][i], s[mt][i + 1]);
-            mx = __builtin_fmaxf(mx, xor32(mx));
-            const float m_new = __builtin_fmaxf(m_run, mx * sl2);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            if (!wave_all(m_new == m_run)) {
-                const float corr = exp2_fast(m_run - m_use);
-                l_run *= corr;
+                    for (int md = 0; md < D / 32; ++md)
 #pragma unroll
-                for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ot[md][i] *= corr;
-            }
-            m_run = m_new;
-            float psum = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = exp2_fast(__builtin_fmaf(s[mt][i], sl2, -m_use));
-                    s[mt][i] = p;
-                    psum += p;
+                        for (int i = 0; i < 16; ++i) ot[nt][md][i] *= corr;
+                    m_run[nt] = m_new;
                 }
-            l_run += psum;
-            // ---- O^T += V^T P^T ----------------------------------------------------
+            }
+            // P in bf16 (the matrix-core operand); l sums the same rounded values
+            // with v_dot2c_f32_bf16 against (1, 1), two per instruction.
+            bf16x8 pb[NT][T::BN / 16];
 #pragma unroll
-            for (int ks = 0; ks < T::BN / 16; ++ks) {
-                const int mt = ks >> 1, base = (ks & 1) * 8;
-                bf16x8 pb;
+            for (int nt = 0; nt < NT; ++nt) {
+                const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
+                float psum = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[mt][base + e];
-                const uint16_t* va = sV + n * T::VS + ks * 16 + hf * 8;
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        bf16x2 pp;
+                        const float p0 = exp2_fast(__builtin_fmaf(s[mt][nt][i], sl2, -m_use));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[mt][nt][i + 1], sl2, -m_use));
+                        pp[0] = (__bf16)p0;
+                        pp[1] = (__bf16)p1;
+                        if (FWD_DOT2)
+                            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
+                        else
+                            psum += p0 + p1;
+                        pb[nt][mt * 2 + (i >> 3)][i & 7] = pp[0];
+                        pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = pp[1];
+                    }
+                l_run[nt] += psum;
+            }
+            // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile) ----------
+#pragma unroll
+            for (int ks = 0; ks < T::BN / 16; ++ks)
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(va + md * 32 * T::VS);
-                    ot[md] = mfma32x32x16(a, pb, ot[md]);
+                    const bf16x8 a = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(a, pb[nt][ks], ot[nt][md]);
                 }
-            }
         }
 
-        if (j + 1 < nblk) {
-            uint16_t* nK = smem + ((j + 1) & 1) * T::STAGE;
-            store_kv_block<D>(st, nK, nK + T::K_ELEMS, tid);
-        }
+        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * T::STAGE);
         __syncthreads();
     }
 
-    // ---- finalise: O = O / l, LSE = (m + log2 l) * ln 2 ---------------------------
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qi < Nq) {
-        uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
+    // ---- finalise: O = O / l, LSE = (m + log2 l) * ln 2 -------------------------------
 #pragma unroll
-        for (int md = 0; md < D / 32; ++md)
+    for (int nt = 0; nt < NT; ++nt) {
+        const int qi = qw + nt * 32 + n;
+        const float l_tot = pair_sum(l_run[nt]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qi < Nq) {
+            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dcol = md * 32 + g * 8 + hf * 4;
-                const uint32_t lo = pack_bf16x2(ot[md][g * 4 + 0] * inv, ot[md][g * 4 + 1] * inv);
-                const uint32_t hi = pack_bf16x2(ot[md][g * 4 + 2] * inv, ot[md][g * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-            }
-        if (hf == 0)
-            LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+            for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dcol = md * 32 + g * 8 + hf * 4;
+                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
+                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
+                }
+            if (hf == 0)
+                LSE[(size_t)(b * Hq + h) * Nq + qi] =
+                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+// Grid: (query-block slot, batch*head) flattened with batch*head fastest, so
+// the blocks of one (batch, head) are BH launch slots apart (the same XCD
+// when BH is a multiple of 8) and share its L2 copy of K and V.  Causal: slot
+// p processes query blocks p and nqb-1-p, so every workgroup does the same
+// amount of work (nqb+1 half-blocks of keys) and no long tail is left.
+template <int D, int NT, bool CAUSAL>
+__global__ __launch_bounds__(256, (D * NT > 128 ? 1 : 2)) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
+    float sl2) {
+    extern __shared__ __align__(16) uint16_t smem[];
+    const int slot = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    const int b = bh / Hq, h = bh % Hq;
+    if (!CAUSAL || !FWD_PAIR) {
+        fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, CAUSAL ? nqb - 1 - slot : slot, sl2,
+                                  smem);
+        return;
+    }
+    const int heavy = nqb - 1 - slot;
+    fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, heavy, sl2, smem);
+    if (slot != heavy) {
+        __syncthreads();
+        fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, slot, sl2, smem);
     }
 }
 
@@ -351,24 +390,25 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int NT, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-    using T = FwdTile<D>;
+    using T = FwdTile<D, NT>;
     const int nqb = (a.Nq + T::BM - 1) / T::BM;
+    const int slots = (CAUSAL && FWD_PAIR) ? (nqb + 1) / 2 : nqb;
     const int BH = a.B * a.Hq;
-    auto kern = fwd_bf16_kernel<D, CAUSAL>;
+    auto kern = fwd_bf16_kernel<D, NT, CAUSAL>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), T::LDS_BYTES, (hipStream_t)a.stream,
+    hipLaunchKernelGGL(kern, dim3(slots * BH), dim3(256), T::LDS_BYTES, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, a.scale * kLog2e);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, true>(a) : launch_fwd_bf16_t<64, false>(a);
-    return a.causal ? launch_fwd_bf16_t<128, true>(a) : launch_fwd_bf16_t<128, false>(a);
+    if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, FWD_NT64, true>(a) : launch_fwd_bf16_t<64, FWD_NT64, false>(a);
+    return a.causal ? launch_fwd_bf16_t<128, FWD_NT128, true>(a) : launch_fwd_bf16_t<128, FWD_NT128, false>(a);
 }
 
 template <int D>

@@ -112,3 +112,10 @@ def test_binding_names_match_header():
     for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
               "fa_abi_version"):
         assert callable(getattr(fa, n))
+
+
+def test_one_hip_runtime_in_the_process(lib):
+    """The binding loads torch's HIP runtime first, so libfa shares it."""
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(hip) == 1, hip
