@@ -116,6 +116,54 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* X, int S, int k0, int 
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---------------------------------------------------------------------------
+// Dense LDS tiles written by direct-to-LDS loads (no padding possible: each
+// load instruction fills 64 consecutive 16-byte slots).  Bank conflicts are
+// avoided instead by an XOR swizzle of the 16-byte chunk index within a row:
+// chunk c of row r lives at slot c ^ swz(r).  swz is chosen so that
+//  * 16 consecutive rows at one chunk (a 16-byte row read by 16 lanes) land in
+//    16 distinct bank quads, and
+//  * 4 consecutive rows x 4 consecutive chunks (one transpose read of a
+//    16-lane group) land in 16 distinct bank quads.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);   // 16 chunks (256 B) per row
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);             // 8 chunks (128 B) per row
+}
+
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int c) {
+    return r * D + ((c ^ swz<D>(r)) << 3);
+}
+
+// frag_rows on a swizzled dense tile [rows][D]
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows_swz(const uint16_t* X, int r0, int c0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(X + swz_off<D>(r0 + (lane & 31), (c0 >> 3) + (lane >> 5)));
+}
+
+// frag_tr on a swizzled dense tile [rows][D] (same lane mapping as frag_tr)
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr_swz(const uint16_t* X, int k0, int c0, int lane) {
+    const int t = lane & 15;
+    const int row = k0 + (lane >> 5) * 4 + (t >> 2);
+    const int col = c0 + ((lane >> 4) & 1) * 16 + (t & 3) * 4;
+    const uint16_t* p0 = X + swz_off<D>(row, col >> 3) + (col & 7);
+    const uint16_t* p1 = X + swz_off<D>(row + 8, col >> 3) + (col & 7);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// s_waitcnt on outstanding vector-memory operations only (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {

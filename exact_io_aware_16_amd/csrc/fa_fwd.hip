@@ -41,6 +41,46 @@
 #ifndef FWD_PAIR
 #define FWD_PAIR 0
 #endif
+// Software-pipelined block loop (1) or the plain one (0).
+#ifndef FWD_PIPE
+#define FWD_PIPE 1
+#endif
+// Direct-to-LDS ring kernel (1) or the register-staged kernels (0), and its
+// waves per workgroup / ring stages per head dimension.
+#ifndef FWD_RING
+#define FWD_RING 1
+#endif
+#ifndef RING_NW64
+#define RING_NW64 4
+#endif
+#ifndef RING_S64
+#define RING_S64 2
+#endif
+#ifndef RING_NW128
+#define RING_NW128 8
+#endif
+#ifndef RING_S128
+#define RING_S128 4
+#endif
+#ifndef RING_NT64
+#define RING_NT64 1
+#endif
+// key groups (of 16) whose V fragments are fetched before the exponentials (d = 64)
+#ifndef RING_VH64
+#define RING_VH64 4
+#endif
+#ifndef RING_NT128
+#define RING_NT128 1
+#endif
+// Explicit instruction schedule of the pipelined loop's overlap region.
+#ifndef FWD_SCHED
+#define FWD_SCHED 1
+#endif
+#if FWD_PIPE
+#define FWD_QBLOCK fwd_qblock_pipe
+#else
+#define FWD_QBLOCK fwd_qblock
+#endif
 // Row sums with v_dot2c_f32_bf16 on the packed bf16 P (1) or float adds (0).
 #ifndef FWD_DOT2
 #define FWD_DOT2 0
@@ -274,6 +314,530 @@ __device__ __forceinline__ void fwd_qblock(const uint16_t* __restrict__ Q, const
     }
 }
 
+// The same pass, software pipelined inside each wave: K is staged one block
+// ahead of V, so while the exponentials of block j run on the vector ALUs the
+// scores of block j+1 are already being produced on the matrix cores (the two
+// are independent and sit in one basic block for the scheduler to interleave),
+// and O^T += V^T P^T of block j follows.  LDS holds two K and two V buffers:
+// during iteration j, K(j+1) and V(j) are read while K(j+2) and V(j+1) are
+// being loaded; one barrier per iteration.
+template <int D, int NT, bool CAUSAL>
+__device__ __forceinline__ void fwd_qblock_pipe(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                                float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b,
+                                                int h, int qb, float sl2, uint16_t* smem) {
+    using T = FwdTile<D, NT>;
+    const int hk = h / (Hq / Hkv);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+
+    const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;
+    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nk * D;
+    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
+
+    const int off = Nk - Nq;
+    const int qw = qb * T::BM + wave * T::QW;
+
+    bf16x8 qf[NT][D / 16];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* qrow = qbase + (size_t)min(qw + nt * 32 + n, Nq - 1) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
+    }
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
+    const int nblk = (kv_end + T::BN - 1) / T::BN;
+    const int wave_end = CAUSAL ? min(Nk, qw + T::QW + off) : Nk;
+    const int mask_from = CAUSAL ? (qw + off) : Nk;
+
+    uint16_t* sKb = smem;                       // two K buffers
+    uint16_t* sVb = smem + 2 * T::K_ELEMS;      // two V buffers
+
+    f32x16 ot[NT][D / 32];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md) ot[nt][md] = zero16();
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+        l_run[nt] = 0.f;
+    }
+
+    u32x4 kr[T::CPT], vr[T::CPT];
+    auto load_k = [&](int key0) {
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            kr[r] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8);
+        }
+    };
+    auto load_v = [&](int key0) {
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            vr[r] = *reinterpret_cast<const u32x4*>(vbase + (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8);
+        }
+    };
+    auto store_k = [&](uint16_t* dst) {
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            *reinterpret_cast<u32x4*>(dst + (c / (D / 8)) * T::KS + (c % (D / 8)) * 8) = kr[r];
+        }
+    };
+    auto store_v = [&](uint16_t* dst) {
+#pragma unroll
+        for (int r = 0; r < T::CPT; ++r) {
+            const int c = tid + 256 * r;
+            *reinterpret_cast<u32x4*>(dst + (c / (D / 8)) * T::VS + (c % (D / 8)) * 8) = vr[r];
+        }
+    };
+    auto scores = [&](const uint16_t* sK, f32x16 (&s)[2][NT]) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const bf16x8 a = frag_rows(sK, T::KS, mt * 32, kk * 16, lane);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(a, qf[nt][kk], s[mt][nt]);
+            }
+        }
+    };
+    // mask + row max + lazy rescale for one block of scores (VALU, may branch)
+    auto prepare = [&](f32x16 (&s)[2][NT], int key0) {
+        if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int qi = qw + nt * 32 + n;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                        const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
+                        s[mt][nt][i] = ok ? s[mt][nt][i] : kNegInf;
+                    }
+            }
+        }
+        float mx[NT];
+        bool grow = false;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            // two independent max3 chains, joined at the end
+            float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                m0 = max3f(m0, s[0][nt][i], s[0][nt][i + 1]);
+                m1 = max3f(m1, s[1][nt][i], s[1][nt][i + 1]);
+            }
+            mx[nt] = pair_max(__builtin_fmaxf(m0, m1)) * sl2;
+            grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
+        }
+        if (!wave_all(!grow)) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
+                const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
+                l_run[nt] *= corr;
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) ot[nt][md][i] *= corr;
+                m_run[nt] = m_new;
+            }
+        }
+    };
+    // exponentials -> bf16 P and the row-sum update (VALU only, no branch)
+    auto exponentiate = [&](const f32x16 (&s)[2][NT], bf16x8 (&pb)[NT][T::BN / 16]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
+            float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = exp2_fast(__builtin_fmaf(s[mt][nt][i], sl2, -m_use));
+                    const float p1 = exp2_fast(__builtin_fmaf(s[mt][nt][i + 1], sl2, -m_use));
+                    ps0 += p0;
+                    ps1 += p1;
+                    pb[nt][mt * 2 + (i >> 3)][i & 7] = (__bf16)p0;
+                    pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)p1;
+                }
+            l_run[nt] += ps0 + ps1;
+        }
+    };
+    auto accumulate = [&](const uint16_t* sV, const bf16x8 (&pb)[NT][T::BN / 16]) {
+#pragma unroll
+        for (int ks = 0; ks < T::BN / 16; ++ks)
+#pragma unroll
+            for (int md = 0; md < D / 32; ++md) {
+                const bf16x8 a = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(a, pb[nt][ks], ot[nt][md]);
+            }
+    };
+
+    // ---- prologue: K(0), V(0), K(1) into LDS; S(0) ----------------------------------
+    load_k(0);
+    load_v(0);
+    store_k(sKb);
+    store_v(sVb);
+    if (nblk > 1) {
+        load_k(T::BN);
+        store_k(sKb + T::K_ELEMS);
+    }
+    __syncthreads();
+    f32x16 s_cur[2][NT], s_nxt[2][NT];
+    if (0 < wave_end) scores(sKb, s_cur);
+
+    for (int j = 0; j < nblk; ++j) {
+        const int key0 = j * T::BN;
+        const bool have_v = j + 1 < nblk, have_k = j + 2 < nblk;
+        if (have_v) load_v(key0 + T::BN);
+        if (have_k) load_k(key0 + 2 * T::BN);
+        const bool do_cur = key0 < wave_end;
+        const bool do_nxt = have_v && key0 + T::BN < wave_end;
+        const uint16_t* sKn = sKb + ((j + 1) & 1) * T::K_ELEMS;
+        const uint16_t* sV = sVb + (j & 1) * T::V_ELEMS;
+        if (do_cur) {
+            prepare(s_cur, key0);
+            bf16x8 pb[NT][T::BN / 16];
+            if (do_nxt && FWD_SCHED && D == 64) {
+                // One basic block, scheduled explicitly: every LDS fragment of
+                // K(j+1) and V(j) is requested first, then each score MFMA of
+                // block j+1 is followed by a group of vector instructions of the
+                // exponentials of block j (the matrix core runs the MFMA while
+                // the wave keeps issuing), then O^T += V^T P^T of block j.
+                constexpr int NKF = 2 * (D / 16), NVF = (T::BN / 16) * (D / 32);
+                bf16x8 kfr[2][D / 16], vfr[T::BN / 16][D / 32];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int kk = 0; kk < D / 16; ++kk) kfr[mt][kk] = frag_rows(sKn, T::KS, mt * 32, kk * 16, lane);
+#pragma unroll
+                for (int ks = 0; ks < T::BN / 16; ++ks)
+#pragma unroll
+                    for (int md = 0; md < D / 32; ++md) vfr[ks][md] = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) s_nxt[mt][nt] = zero16();
+#pragma unroll
+                    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            s_nxt[mt][nt] = mfma32x32x16(kfr[mt][kk], qf[nt][kk], s_nxt[mt][nt]);
+                }
+                exponentiate(s_cur, pb);
+#pragma unroll
+                for (int ks = 0; ks < T::BN / 16; ++ks)
+#pragma unroll
+                    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            ot[nt][md] = mfma32x32x16(vfr[ks][md], pb[nt][ks], ot[nt][md]);
+                // schedule: LDS reads, a few VALU, then (MFMA, VALU group) pairs
+                constexpr int NQK = 2 * (D / 16) * NT;
+                constexpr int VPER = (120 * NT + NQK - 1) / NQK;
+                __builtin_amdgcn_sched_group_barrier(0x100, NKF + 2 * NVF, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+                static_for<0, NQK>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, VPER, 0);
+                });
+                __builtin_amdgcn_sched_group_barrier(0x008, (T::BN / 16) * (D / 32) * NT, 0);
+            } else {
+                if (do_nxt) scores(sKn, s_nxt);
+                exponentiate(s_cur, pb);
+                accumulate(sV, pb);
+            }
+        }
+        if (have_v) store_v(sVb + ((j + 1) & 1) * T::V_ELEMS);
+        if (have_k) store_k(sKb + (j & 1) * T::K_ELEMS);
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) s_cur[mt][nt] = s_nxt[mt][nt];
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int qi = qw + nt * 32 + n;
+        const float l_tot = pair_sum(l_run[nt]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qi < Nq) {
+            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
+#pragma unroll
+            for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dcol = md * 32 + g * 8 + hf * 4;
+                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
+                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
+                }
+            if (hf == 0)
+                LSE[(size_t)(b * Hq + h) * Nq + qi] =
+                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ring variant: K/V blocks travel global -> LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4, no register staging) into a ring of S stages, so
+// S-1 blocks are in flight while one is computed.  The block loop is bound by
+// load latency otherwise: a block's compute is far shorter than a round trip
+// to L2/HBM.  Tiles are dense and XOR-swizzled (see swz()).  Per block: wait
+// for this wave's loads of the block (vmcnt), one barrier (all waves' loads
+// landed, and everybody finished the block that the next load overwrites),
+// issue the load S-1 blocks ahead, compute.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int S, int NT>
+struct RingTile {
+    static constexpr int QW = 32 * NT;             // query rows per wave
+    static constexpr int BM = QW * NW;             // query rows per workgroup
+    static constexpr int BN = 64;                  // keys per block
+    static constexpr int TILE = BN * D;            // elements of one K (or V) block
+    static constexpr int STAGE = 2 * TILE;         // K then V
+    static constexpr int LDS_BYTES = S * STAGE * 2;
+    static constexpr int IPW = (BN * D / 8) / 64 / NW;   // load instructions per wave per tile
+    static constexpr int LPS = 2 * IPW;                  // per wave per stage (K and V)
+    static_assert(IPW >= 1 && (BN * D / 8) % (64 * NW) == 0, "tile must split evenly over the waves");
+};
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D, int NW, int S, int NT, bool CAUSAL>
+__device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                                float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b,
+                                                int h, int qb, float sl2, uint16_t* smem) {
+    using T = RingTile<D, NW, S, NT>;
+    const int hk = h / (Hq / Hkv);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+
+    const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;
+    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nk * D;
+    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
+
+    const int off = Nk - Nq;
+    const int qw = qb * T::BM + wave * T::QW;
+
+    // Q^T as the B operand (column tile nt: query qw + 32 nt + n); rows past Nq
+    // read row Nq - 1 and are never stored.
+    bf16x8 qf[NT][D / 16];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* qrow = qbase + (size_t)min(qw + nt * 32 + n, Nq - 1) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
+    }
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
+    const int nblk = (kv_end + T::BN - 1) / T::BN;
+    const int wave_end = CAUSAL ? min(Nk, qw + T::QW + off) : Nk;
+    const int mask_from = CAUSAL ? (qw + off) : Nk;
+
+    // Issue this wave's share of block `blk` into stage `st` (rows clamped to
+    // kv_end - 1: always in bounds).  Lane l of load i writes slot
+    // (wave*IPW + i)*64 + l of the tile: row = slot / (D/8), swizzled chunk
+    // slot % (D/8), i.e. global chunk (slot % (D/8)) ^ swz(row).
+    auto issue = [&](int blk, int st) {
+        uint16_t* kt = smem + st * T::STAGE;
+        uint16_t* vt = kt + T::TILE;
+#pragma unroll
+        for (int i = 0; i < T::IPW; ++i) {
+            const int slot = (wave * T::IPW + i) * 64 + lane;
+            const int row = slot / (D / 8), pos = slot % (D / 8);
+            const size_t g = (size_t)min(blk * T::BN + row, kv_end - 1) * D + ((pos ^ swz<D>(row)) << 3);
+            const int lds_off = (wave * T::IPW + i) * 64 * 8;   // elements; wave-uniform
+            __builtin_amdgcn_global_load_lds(kbase + g, LDS_PTR(kt + lds_off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + g, LDS_PTR(vt + lds_off), 16, 0, 0);
+        }
+    };
+
+    f32x16 ot[NT][D / 32];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md) ot[nt][md] = zero16();
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+        l_run[nt] = 0.f;
+    }
+
+    // prologue: blocks 0 .. S-2 (always S-1 stages issued, so the wait count is static)
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) issue(st, st);
+
+    for (int j = 0; j < nblk; ++j) {
+        const int st = j % S;
+        // this wave's loads of block j are done once at most (S-2) stages remain outstanding
+        wait_vmcnt<(S - 2) * T::LPS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + S - 1, (j + S - 1) % S);
+
+        const int key0 = j * T::BN;
+        if (key0 < wave_end) {
+            const uint16_t* sK = smem + st * T::STAGE;
+            const uint16_t* sV = sK + T::TILE;
+            // ---- S^T = K Q^T ----------------------------------------------------------
+            // K fragments of a 32-key half are requested before its MFMAs, so LDS
+            // latency is paid once per half; each fragment feeds NT MFMAs.
+            f32x16 s[2][NT];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                bf16x8 kf[D / 16];
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag_rows_swz<D>(sK, mt * 32, kk * 16, lane);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(kf[kk], qf[nt][kk], s[mt][nt]);
+            }
+            // ---- mask (diagonal / tail blocks only) ---------------------------------------
+            if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int qi = qw + nt * 32 + n;
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                            const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
+                            s[mt][nt][i] = ok ? s[mt][nt][i] : kNegInf;
+                        }
+                }
+            }
+            // ---- row max, lazy rescale ------------------------------------------------------
+            float mx[NT];
+            bool grow = false;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    m0 = max3f(m0, s[0][nt][i], s[0][nt][i + 1]);
+                    m1 = max3f(m1, s[1][nt][i], s[1][nt][i + 1]);
+                }
+                mx[nt] = pair_max(__builtin_fmaxf(m0, m1)) * sl2;
+                grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
+            }
+            if (!wave_all(!grow)) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
+                    const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
+                    l_run[nt] *= corr;
+#pragma unroll
+                    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) ot[nt][md][i] *= corr;
+                    m_run[nt] = m_new;
+                }
+            }
+            // V fragments of the first key groups are requested before the
+            // exponentials so their latency hides behind the vector work.
+            constexpr int VH = (D * NT == 64) ? RING_VH64 : 1;
+            bf16x8 vf[VH][D / 32];
+#pragma unroll
+            for (int ks = 0; ks < VH; ++ks)
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md) vf[ks][md] = frag_tr_swz<D>(sV, ks * 16, md * 32, lane);
+            // ---- P = exp2(s*scale*log2e - m) in bf16, row sums ------------------------------
+            bf16x8 pb[NT][T::BN / 16];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
+                float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        const float p0 = exp2_fast(__builtin_fmaf(s[mt][nt][i], sl2, -m_use));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[mt][nt][i + 1], sl2, -m_use));
+                        ps0 += p0;
+                        ps1 += p1;
+                        pb[nt][mt * 2 + (i >> 3)][i & 7] = (__bf16)p0;
+                        pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)p1;
+                    }
+                l_run[nt] += ps0 + ps1;
+            }
+            // ---- O^T += V^T P^T -------------------------------------------------------------
+#pragma unroll
+            for (int ks = 0; ks < T::BN / 16; ++ks) {
+                bf16x8 va[D / 32];
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md)
+                    va[md] = ks < VH ? vf[ks < VH ? ks : 0][md] : frag_tr_swz<D>(sV, ks * 16, md * 32, lane);
+#pragma unroll
+                for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(va[md], pb[nt][ks], ot[nt][md]);
+            }
+        }
+    }
+    // drain the ring's trailing loads before the workgroup's LDS is reused
+    wait_vmcnt<0>();
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int qi = qw + nt * 32 + n;
+        const float l_tot = pair_sum(l_run[nt]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qi < Nq) {
+            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
+#pragma unroll
+            for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dcol = md * 32 + g * 8 + hf * 4;
+                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
+                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
+                }
+            if (hf == 0)
+                LSE[(size_t)(b * Hq + h) * Nq + qi] =
+                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+template <int D, int NW, int S, int NT, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, ((NW == 4 && D * NT <= 128) ? 2 : 1)) void fwd_ring_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
+    float sl2) {
+    extern __shared__ __align__(16) uint16_t smem[];
+    const int slot = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    fwd_qblock_ring<D, NW, S, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, bh / Hq, bh % Hq,
+                                          CAUSAL ? nqb - 1 - slot : slot, sl2, smem);
+}
+
 // Grid: (query-block slot, batch*head) flattened with batch*head fastest, so
 // the blocks of one (batch, head) are BH launch slots apart (the same XCD
 // when BH is a multiple of 8) and share its L2 copy of K and V.  Causal: slot
@@ -289,15 +853,15 @@ __global__ __launch_bounds__(256, (D * NT > 128 ? 1 : 2)) void fwd_bf16_kernel(
     const int bh = blockIdx.x % BH;
     const int b = bh / Hq, h = bh % Hq;
     if (!CAUSAL || !FWD_PAIR) {
-        fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, CAUSAL ? nqb - 1 - slot : slot, sl2,
+        FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, CAUSAL ? nqb - 1 - slot : slot, sl2,
                                   smem);
         return;
     }
     const int heavy = nqb - 1 - slot;
-    fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, heavy, sl2, smem);
+    FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, heavy, sl2, smem);
     if (slot != heavy) {
         __syncthreads();
-        fwd_qblock<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, slot, sl2, smem);
+        FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, slot, sl2, smem);
     }
 }
 
@@ -406,7 +970,29 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
     return hipGetLastError();
 }
 
+template <int D, int NW, int S, int NT, bool CAUSAL>
+static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
+    using T = RingTile<D, NW, S, NT>;
+    const int nqb = (a.Nq + T::BM - 1) / T::BM;
+    const int BH = a.B * a.Hq;
+    auto kern = fwd_ring_kernel<D, NW, S, NT, CAUSAL>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                       a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
+#if FWD_RING
+    if (a.d == 64)
+        return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, true>(a)
+                        : launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, false>(a);
+    return a.causal ? launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, true>(a)
+                    : launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, false>(a);
+#endif
     if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, FWD_NT64, true>(a) : launch_fwd_bf16_t<64, FWD_NT64, false>(a);
     return a.causal ? launch_fwd_bf16_t<128, FWD_NT128, true>(a) : launch_fwd_bf16_t<128, FWD_NT128, false>(a);
 }
