@@ -22,7 +22,6 @@ fa_status_t check_scale(float scale) {
 
 fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-size_t decode_nsplit(int Nmax) { return (size_t)((Nmax + fa::kDecodeSplit - 1) / fa::kDecodeSplit); }
 
 }  // namespace
 
@@ -88,10 +87,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d) {
-    (void)Hkv;
-    if (B < 1 || Hq < 1 || Nmax < 1 || d < 1) return 0;
-    const size_t rows = (size_t)B * Hq * decode_nsplit(Nmax);
-    return rows * (size_t)d * sizeof(float) + rows * sizeof(float);
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nmax < 1 || d < 1 || Hq % Hkv != 0) return 0;
+    return fa::decode_workspace_bytes(B, Hq, Hkv, Nmax, d);
 }
 
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens, void* o,
@@ -113,11 +110,10 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, c
         fa::FwdArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, 1, Nmax, d, scale, 0, stream};
         return from_hip(fa::launch_fwd_f32(a, seqlens));
     }
-    const size_t nsplit = decode_nsplit(Nmax);
-    float* part_o = static_cast<float*>(workspace);
-    float* part_lse = part_o + (size_t)B * Hq * nsplit * d;
-    fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nmax, d, scale, part_o, part_lse,
-                     (int)nsplit, stream};
+    fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nmax, d, scale, nullptr, nullptr,
+                     nullptr, stream};
+    float* ws = static_cast<float*>(workspace);
+    fa::decode_workspace_layout(a, ws);
     return from_hip(fa::launch_decode_bf16(a));
 }
 

@@ -4,21 +4,22 @@
 // page, sections 3.1 MQA and 3.2 GQA).
 //
 // The work is bound by reading the cache once.  MI355X mapping:
-//  * split-K over the cache: workgroup (split s, K/V head, batch) streams keys
-//    [512 s, 512 s + 512) of one K/V head exactly once, for all query heads of
-//    its group at the same time (up to 32 heads in one matrix-core column
-//    tile), so the grouped heads cost no extra cache traffic;
-//  * 128-key sub-blocks are loaded with fully coalesced 16-byte loads into
-//    registers one sub-block ahead, then staged through LDS (K as is, V
-//    transposed) for the 32x32x16 bf16 matrix cores; each wave owns 32 keys;
-//  * splits past a sequence's length exit at once; keys at or past the length
-//    are never read into the result (their V rows are replaced by zeros and
-//    their scores by -inf), so any contents there, NaN included, are harmless;
-//  * each split ends with the four waves' (max, sum, output) merged in LDS and
-//    one partial (O_s, lse_s) written; a second kernel merges the splits with
-//    weights exp(lse_s - lse), the same rescaling the online softmax applies
-//    when a new block arrives (holysheep.ai Flash Attention article, section
-//    2.1 Online Softmax).
+//  * every cached key row is read exactly once, for all query heads of its
+//    group at the same time (up to 32 heads in one matrix-core column tile),
+//    so grouped heads cost no extra cache traffic;
+//  * stream-K work split: the rows' keys are cut into 32-key stages laid end
+//    to end and each one-wave workgroup takes an equal contiguous share, so
+//    ragged sequence lengths leave no wave idle and no tail of short splits;
+//  * each wave streams its share through a private ring of LDS stages filled
+//    by direct-to-LDS loads (global_load_lds_dwordx4) ahead of the 32x32x16
+//    bf16 matrix cores, with explicit vmcnt waits and no barriers;
+//  * keys at or past a sequence's length are never read into the result (the
+//    row is clamped to the last valid key and its score masked to -inf), so
+//    any cache contents there, NaN included, are harmless;
+//  * each wave writes one partial (O_s, lse_s) per row piece it covered; a
+//    second kernel merges a row's pieces with weights exp(lse_s - lse), the
+//    same rescaling the online softmax applies when a new block arrives
+//    (holysheep.ai Flash Attention article, section 2.1 Online Softmax).
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -27,186 +28,8 @@
 namespace fa {
 
 namespace {
-
-constexpr int DBN = 128;  // keys per sub-block (4 waves x 32)
-
-template <int D>
-struct DecTile {
-    static constexpr int KS = D + 8;    // K row stride (row reads: distinct bank quads)
-    static constexpr int VS = D + 32;   // V row stride (64 B mod 256 B: transpose reads 2-way)
-    static constexpr int K_ELEMS = DBN * KS;
-    static constexpr int V_ELEMS = DBN * VS;
-    static constexpr int LDS_BYTES = (K_ELEMS + V_ELEMS) * 2;
-    static constexpr int CPT = DBN * D / 8 / 256;   // 16-byte chunks per thread per tensor
-};
-
 constexpr float kRescaleThreshold = 8.0f;   // lazy rescaling, as in the forward kernel
-
 }  // namespace
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv,
-    int Nmax, int nsplit, int nht, float sl2) {
-    using T = DecTile<D>;
-    extern __shared__ __align__(16) uint16_t smem[];
-    uint16_t* sK = smem;
-    uint16_t* sV = smem + T::K_ELEMS;
-
-    const int s = blockIdx.x;
-    const int hk = blockIdx.y / nht, ht = blockIdx.y % nht;
-    const int b = blockIdx.z;
-    const int g = Hq / Hkv;
-    const int len = max(0, min(Nmax, seqlens[b]));
-    const int k_begin = s * kDecodeSplit;
-    if (k_begin >= len) return;
-    const int k_end = min(len, k_begin + kDecodeSplit);
-    const int nsub = (k_end - k_begin + DBN - 1) / DBN;
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 31, hf = lane >> 5;
-    const int gh = ht * 32 + n;          // head index inside the group
-    const int hq = hk * g + gh;
-    const bool head_ok = gh < g;
-
-    bf16x8 qf[D / 16];
-    {
-        // lanes past the group's last head read that head's row; never stored
-        const uint16_t* qrow = Q + (size_t)(b * Hq + (head_ok ? hq : hk * g + g - 1)) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
-    }
-
-    const uint16_t* kb = K + (size_t)(b * Hkv + hk) * Nmax * D;
-    const uint16_t* vb = V + (size_t)(b * Hkv + hk) * Nmax * D;
-
-    // Keys at or past k_end are read from row k_end - 1 (a valid, finite row of
-    // this sequence): their scores are masked to -inf so they carry weight
-    // exactly 0, and the cache beyond the sequence length is never touched.
-    // 16 consecutive threads move one 256-byte key row (full-row loads, one
-    // contiguous LDS run per row).
-    u32x4 kr[T::CPT], vr[T::CPT];
-    auto load = [&](int key0) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            const size_t gi = (size_t)min(key0 + row, k_end - 1) * D + col8 * 8;
-            kr[r] = *reinterpret_cast<const u32x4*>(kb + gi);
-            vr[r] = *reinterpret_cast<const u32x4*>(vb + gi);
-        }
-    };
-    auto store = [&]() {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            *reinterpret_cast<u32x4*>(sK + row * T::KS + col8 * 8) = kr[r];
-            *reinterpret_cast<u32x4*>(sV + row * T::VS + col8 * 8) = vr[r];
-        }
-    };
-
-    f32x16 ot[D / 32];
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md) ot[md] = zero16();
-    float m_run = kNegInf, l_run = 0.f;
-
-    load(k_begin);
-    for (int it = 0; it < nsub; ++it) {
-        const int key0 = k_begin + it * DBN;
-        store();
-        __syncthreads();
-        if (it + 1 < nsub) load(key0 + DBN);
-        const int wkey0 = key0 + wave * 32;
-        if (wkey0 < k_end) {
-            f32x16 sc = zero16();
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                sc = mfma32x32x16(frag_rows(sK, T::KS, wave * 32, kk * 16, lane), qf[kk], sc);
-            if (wkey0 + 32 > k_end) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = wkey0 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                    sc[i] = key < k_end ? sc[i] : kNegInf;
-                }
-            }
-            float mx = kNegInf;
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = max3f(mx, sc[i], sc[i + 1]);
-            mx = pair_max(mx) * sl2;
-            if (!wave_all(mx <= m_run + kRescaleThreshold)) {
-                const float m_new = __builtin_fmaxf(m_run, mx);
-                const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
-                l_run *= corr;
-#pragma unroll
-                for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ot[md][i] *= corr;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -m_use));
-                sc[i] = p;
-                l_run += p;
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 pb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[ks * 8 + e];
-#pragma unroll
-                for (int md = 0; md < D / 32; ++md)
-                    ot[md] = mfma32x32x16(frag_tr(sV, T::VS, wave * 32 + ks * 16, md * 32, lane), pb, ot[md]);
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- merge the four waves' partial softmax states in LDS ------------------
-    float* sm = reinterpret_cast<float*>(smem);   // [4][32] max
-    float* sl = sm + 128;                         // [4][32] sum
-    float* so = sl + 128;                         // [4][32][D] scaled outputs
-    const float l_tot = pair_sum(l_run);
-    if (hf == 0) {
-        sm[wave * 32 + n] = m_run;
-        sl[wave * 32 + n] = l_tot;
-    }
-    __syncthreads();
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, sm[w * 32 + n]);
-    const float wscale = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - M);
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int dcol = md * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-            so[(wave * 32 + n) * D + dcol] = ot[md][i] * wscale;
-        }
-    __syncthreads();
-    for (int e = tid; e < 32 * D; e += 256) {
-        const int hn = e / D, dcol = e % D;
-        const int ghn = ht * 32 + hn;
-        if (ghn >= g) continue;
-        float Mn = kNegInf;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) Mn = __builtin_fmaxf(Mn, sm[w * 32 + hn]);
-        float L = 0.f, acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = sm[w * 32 + hn];
-            L += (mw == kNegInf) ? 0.f : sl[w * 32 + hn] * exp2_fast(mw - Mn);
-            acc += so[(w * 32 + hn) * D + dcol];
-        }
-        const size_t row = (size_t)(b * Hq + hk * g + ghn) * nsplit + s;
-        part_o[row * D + dcol] = acc / L;
-        if (dcol == 0) part_lse[row] = (Mn + log2_fast(L)) * kLn2;
-    }
-}
 
 // All V^T fragments of one 32-key stage (frag_tr_swz for k0 = 0, 16 and every
 // 32-column block), read with ds_read_b64_tr_b16 in a single asm block that
@@ -267,32 +90,6 @@ __device__ __forceinline__ void stage_vt_frags(const uint16_t* X, int lane, bf16
     }
 }
 
-// ---------------------------------------------------------------------------
-// Streaming split kernel.  A workgroup is one wave and owns one split
-// (keys [512 c, 512 c + 512) of one K/V head of one sequence, for up to 32
-// query heads of its group).  The split is streamed in 32-key stages through
-// a private ring of DS stages in LDS, filled by direct-to-LDS loads
-// (global_load_lds_dwordx4) DS-1 stages ahead of the matrix cores; the wave
-// only reads what it loaded itself, so no barriers are needed, and the loop
-// issues no register-destination loads, so every wait is an explicit vmcnt.
-// Several such waves share a CU and the hardware dispatcher hands out splits
-// as waves finish, which balances ragged sequence lengths.  K and V stages are
-// dense and XOR-swizzled (conflict-free row and transpose reads).
-// ---------------------------------------------------------------------------
-template <int D, int DS, int QR>
-struct RingDecTile {
-    static constexpr int BK = 32;                    // keys per stage
-    static constexpr int TILE = BK * D;              // elements of K (or V) per stage
-    static constexpr int STAGE = 2 * TILE;
-    static constexpr int QTILE = QR * D;             // the group's query rows, loaded once
-    static constexpr int LDS_BYTES = (DS * STAGE + QTILE) * 2;
-    static constexpr int IPT = BK * D / 8 / 64;      // load instructions per K (or V) tile
-    static constexpr int QI = QR * D / 8 / 64;       // load instructions for the query rows
-    static constexpr int LPS = 2 * IPT;              // per stage
-    static_assert(QI >= 1 && QR * D / 8 == QI * 64, "query rows must fill whole loads");
-    static_assert((DS - 1) * LPS < 64, "vmcnt range");
-};
-
 #define DEC_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // wait until at most r stages (r < DS-1, runtime) are still in flight
@@ -304,85 +101,190 @@ __device__ __forceinline__ void wait_stages(int r) {
     wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K variant.  The key range of every (sequence, K/V head, head tile)
+// row is cut into 32-key stages and all stages of all rows are laid end to
+// end; wave w of G takes the contiguous range [w S / G, (w+1) S / G) of the S
+// stages, so every wave streams the same number of bytes whatever the mix of
+// sequence lengths, and its ring of DS stages runs across row boundaries
+// without draining.  A stage holds 32 keys of K and V and the row's query
+// rows (dense, XOR-swizzled), all brought in by direct-to-LDS loads DS-1
+// stages ahead.  At the end of a row, or of its range, a wave writes the
+// partial (O_s, lse_s) of the stages it saw to slot r + w (row r, wave w):
+// the waves touching one row are consecutive, so these slots never collide
+// and there are at most rows + G of them.  Wave 0 also writes the prefix sums
+// of stages per sequence, from which the combine finds each row's waves.
+// ---------------------------------------------------------------------------
 template <int D, int DS, int QR>
-__global__ __launch_bounds__(64) void decode_ring_kernel(
+struct StreamTile {
+    static constexpr int BK = 32;                    // keys per stage
+    static constexpr int TILE = BK * D;              // elements of K (or V) per stage
+    static constexpr int QTILE = QR * D;             // query rows per stage
+    static constexpr int STAGE = 2 * TILE + QTILE;
+    static constexpr int LDS_BYTES = DS * STAGE * 2;
+    static constexpr int IPT = BK * D / 8 / 64;      // load instructions per K (or V) tile
+    static constexpr int QI = QR * D / 8 / 64;       // load instructions for the query rows
+    static constexpr int LPS = 2 * IPT;              // K and V loads per stage
+    static_assert(QI >= 1 && QR * D / 8 == QI * 64, "query rows must fill whole loads");
+    static_assert((DS - 2) * LPS < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// position in the stage sequence: sequence b (clamped length len, nb stages
+// per row), row ri of that sequence's HK rows, stage j of that row
+struct StreamCursor {
+    int b, len, nb, ri, j;
+};
+
+template <int D, int DS, int QR>
+__global__ __launch_bounds__(64) void decode_stream_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv,
-    int Nmax, int nsplit, int nht, float sl2) {
-    using T = RingDecTile<D, DS, QR>;
+    const int* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int* __restrict__ meta, int B, int Hq, int Hkv, int Nmax, int nht, int G, float sl2) {
+    using T = StreamTile<D, DS, QR>;
     static_assert(DS <= 5, "wait_stages covers at most five stages");
     extern __shared__ __align__(16) uint16_t smem[];
-    const int c = blockIdx.x;
-    const int hk = blockIdx.y / nht, ht = blockIdx.y % nht;
-    const int b = blockIdx.z;
-    const int g = Hq / Hkv;
-    const int len = max(0, min(Nmax, seqlens[b]));
-    const int k_begin = c * kDecodeSplit;
-    if (k_begin >= len) return;
-    const int k_end = min(len, k_begin + kDecodeSplit);
-    const int nst = (k_end - k_begin + T::BK - 1) / T::BK;
-
     const int lane = threadIdx.x;
     const int n = lane & 31, hf = lane >> 5;
-    const int gh = ht * 32 + n;
-    const bool head_ok = gh < g;
-    uint16_t* sQ = smem + DS * T::STAGE;
+    const int g = Hq / Hkv;
+    const int HK = Hkv * nht;                    // rows per sequence
+    const int TR = min(g, 32);                   // partial rows per slot
+    const int w = blockIdx.x;
+    auto clen = [&](int b) { return max(0, min(Nmax, seqlens[b])); };
+    // the same for a wave-uniform b (a scalar load)
+    auto clen_u = [&](int b) { return max(0, min(Nmax, seqlens[__builtin_amdgcn_readfirstlane(b)])); };
 
-    // the group's query rows ht*32 .. ht*32+QR-1 (rows past the group read its
-    // last head; they only feed output columns that are never stored)
-#pragma unroll
-    for (int i = 0; i < T::QI; ++i) {
-        const int slot = i * 64 + lane;
-        const int row = slot / (D / 8), pos = slot % (D / 8);
-        const int head = min(ht * 32 + row, g - 1);
-        const size_t gi = (size_t)(b * Hq + hk * g + head) * D + ((pos ^ swz<D>(row)) << 3);
-        __builtin_amdgcn_global_load_lds(Q + gi, DEC_LDS_PTR(sQ + i * 64 * 8), 16, 0, 0);
+    // total stage count S; wave 0 records the exclusive prefix per sequence
+    int S = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        const int cnt = b < B ? (clen(b) + T::BK - 1) / T::BK * HK : 0;
+        const int incl = wave_incl_scan(cnt, lane);
+        if (w == 0 && b < B) meta[b] = S + incl - cnt;
+        S += __shfl(incl, 63, 64);
     }
+    S = __builtin_amdgcn_readfirstlane(S);
+    if (w == 0 && lane == 0) meta[B] = S;
+    const int s0 = (int)((long long)w * S / G);
+    const int s1 = (int)((long long)(w + 1) * S / G);
+    const int total = s1 - s0;
+    if (total <= 0) return;
 
-    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nmax * D;
-    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nmax * D;
-    // stage j -> ring slot j % DS; keys at or past k_end are read from row
-    // k_end - 1 (their scores are masked to -inf, so they weigh exactly 0)
-    auto issue = [&](int j) {
-        uint16_t* kt = smem + (j % DS) * T::STAGE;
+    // the sequence holding stage s0, and s0's offset inside it
+    int b_st = 0, off = 0;
+    {
+        int run = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int b = b0 + lane;
+            const int cnt = b < B ? (clen(b) + T::BK - 1) / T::BK * HK : 0;
+            const int incl = wave_incl_scan(cnt, lane);
+            const int excl = run + incl - cnt;
+            const unsigned long long m = __ballot(cnt > 0 && excl <= s0 && s0 < excl + cnt);
+            if (m) {
+                const int l = __ffsll((long long)m) - 1;
+                b_st = b0 + l;
+                off = s0 - __shfl(excl, l, 64);
+                break;
+            }
+            run += __shfl(incl, 63, 64);
+        }
+    }
+    StreamCursor start;
+    start.b = __builtin_amdgcn_readfirstlane(b_st);
+    start.len = clen_u(start.b);
+    start.nb = (start.len + T::BK - 1) / T::BK;
+    off = __builtin_amdgcn_readfirstlane(off);
+    start.ri = off / start.nb;
+    start.j = off % start.nb;
+
+    auto advance = [&](StreamCursor& c) {
+        if (++c.j < c.nb) return;
+        c.j = 0;
+        if (++c.ri < HK) return;
+        c.ri = 0;
+        do {
+            if (++c.b >= B) return;   // past the last stage; never used
+            c.len = clen_u(c.b);
+            c.nb = (c.len + T::BK - 1) / T::BK;
+        } while (c.nb == 0);
+    };
+
+    // Stage k goes to ring slot k % DS.  The row's query rows come along with
+    // its first stage in this wave (a row start, or the wave's first stage),
+    // issued before the stage's K and V loads: loads complete in order, so a
+    // wait that leaves only r stages' K and V loads in flight also covers
+    // every query load older than them, and the wait counts stay constant.
+    // Keys at or past the sequence end are read from its last row (their
+    // scores are masked to -inf); query rows past the group read its last head.
+    auto issue = [&](const StreamCursor& c, int k) {
+        uint16_t* kt = smem + (k % DS) * T::STAGE;
         uint16_t* vt = kt + T::TILE;
-        const int key0 = k_begin + j * T::BK;
+        uint16_t* qt = vt + T::TILE;
+        const int hk = c.ri / nht, ht = c.ri % nht;
+        if (c.j == 0 || k == 0) {
+#pragma unroll
+            for (int i = 0; i < T::QI; ++i) {
+                const int slot = i * 64 + lane;
+                const int row = slot / (D / 8), pos = slot % (D / 8);
+                const int head = min(ht * 32 + row, g - 1);
+                const size_t gi = (size_t)(c.b * Hq + hk * g + head) * D + ((pos ^ swz<D>(row)) << 3);
+                __builtin_amdgcn_global_load_lds(Q + gi, DEC_LDS_PTR(qt + i * 64 * 8), 16, 0, 0);
+            }
+        }
+        const int key0 = c.j * T::BK;
+        const uint16_t* kbase = K + (size_t)(c.b * Hkv + hk) * Nmax * D;
+        const uint16_t* vbase = V + (size_t)(c.b * Hkv + hk) * Nmax * D;
 #pragma unroll
         for (int i = 0; i < T::IPT; ++i) {
             const int slot = i * 64 + lane;
             const int row = slot / (D / 8), pos = slot % (D / 8);
-            const size_t gi = (size_t)min(key0 + row, k_end - 1) * D + ((pos ^ swz<D>(row)) << 3);
+            const size_t gi = (size_t)min(key0 + row, c.len - 1) * D + ((pos ^ swz<D>(row)) << 3);
             __builtin_amdgcn_global_load_lds(kbase + gi, DEC_LDS_PTR(kt + i * 64 * 8), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vbase + gi, DEC_LDS_PTR(vt + i * 64 * 8), 16, 0, 0);
         }
     };
-    const int pro = min(DS - 1, nst);
-    for (int j = 0; j < pro; ++j) issue(j);
 
-    // query operand Q^T: lane (n, hf) takes query row min(n, QR-1); the query
-    // loads are the oldest, so waiting down to the prologue's stages suffices
-    wait_stages<T::LPS, DS + 1>(pro);
-    bf16x8 qf[D / 16];
-    {
-        const int qr = min(n, QR - 1);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[kk] = *reinterpret_cast<const bf16x8*>(sQ + swz_off<D>(qr, kk * 2 + hf));
+    StreamCursor ic = start, cc = start;
+    const int pro = min(DS - 1, total);
+    for (int k = 0; k < pro; ++k) {
+        issue(ic, k);
+        advance(ic);
     }
+    bf16x8 qf[D / 16];
 
     f32x16 ot[D / 32];
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) ot[md] = zero16();
     float m_run = kNegInf, l_run = 0.f;
 
-    for (int j = 0; j < nst; ++j) {
-        // stage j has landed once at most min(DS-2, nst-1-j) younger stages remain
-        wait_stages<T::LPS, DS>(min(DS - 2, nst - 1 - j));
+    for (int k = 0; k < total; ++k) {
+        // stage k has landed once at most min(DS-2, total-1-k) younger stages remain
+        wait_stages<T::LPS, DS>(min(DS - 2, total - 1 - k));
         __builtin_amdgcn_sched_barrier(0);
-        if (j + DS - 1 < nst) issue(j + DS - 1);
-        const uint16_t* sK = smem + (j % DS) * T::STAGE;
+        if (k + DS - 1 < total) {
+            issue(ic, k + DS - 1);
+            advance(ic);
+        }
+        const uint16_t* sK = smem + (k % DS) * T::STAGE;
         const uint16_t* sV = sK + T::TILE;
-        const int key0 = k_begin + j * T::BK;
+        const uint16_t* sQ = sV + T::TILE;
+        const int key0 = cc.j * T::BK;
+        const int k_end = cc.len;
+        if (cc.j == 0 || k == 0) {
+            // Q^T operand of the row: lane (n, hf) takes query row min(n, QR-1)
+            const int qr = min(n, QR - 1);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                qf[kk] = *reinterpret_cast<const bf16x8*>(sQ + swz_off<D>(qr, kk * 2 + hf));
+        }
         bf16x8 kf[D / 16];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag_rows_swz<D>(sK, 0, kk * 16, lane);
@@ -432,106 +334,131 @@ __global__ __launch_bounds__(64) void decode_ring_kernel(
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int md = 0; md < D / 32; ++md) ot[md] = mfma32x32x16(vf[ks][md], pb[ks], ot[md]);
-    }
 
-    // the split's partial: O_s = O / l, lse_s = m + log l
-    const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (head_ok) {
-        const size_t row = (size_t)(b * Hq + hk * g + gh) * nsplit + c;
-        float* po = part_o + row * D;
+        if (cc.j == cc.nb - 1 || k == total - 1) {
+            // partial of this row over the stages this wave saw: O / l, m + log l
+            const int hk = cc.ri / nht, ht = cc.ri % nht;
+            const int gh = ht * 32 + n;
+            const float l_tot = pair_sum(l_run);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (gh < g) {
+                const size_t slot = (size_t)(cc.b * HK + cc.ri + w) * TR + n;
+                float* po = part_o + slot * D;
 #pragma unroll
-        for (int md = 0; md < D / 32; ++md)
+                for (int md = 0; md < D / 32; ++md)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<f32x4*>(po + md * 32 + q4 * 8 + hf * 4) =
-                    f32x4{ot[md][q4 * 4] * inv, ot[md][q4 * 4 + 1] * inv, ot[md][q4 * 4 + 2] * inv,
-                          ot[md][q4 * 4 + 3] * inv};
-        if (hf == 0) part_lse[row] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *reinterpret_cast<f32x4*>(po + md * 32 + q4 * 8 + hf * 4) =
+                            f32x4{ot[md][q4 * 4] * inv, ot[md][q4 * 4 + 1] * inv, ot[md][q4 * 4 + 2] * inv,
+                                  ot[md][q4 * 4 + 3] * inv};
+                if (hf == 0) part_lse[slot] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+            }
+            (void)hk;
+#pragma unroll
+            for (int md = 0; md < D / 32; ++md) ot[md] = zero16();
+            m_run = kNegInf;
+            l_run = 0.f;
+        }
+        advance(cc);
     }
 }
 
+// Merge the partials of each (sequence, query head): the row's stages
+// [P, P + nb) were covered by waves wave_of(P) .. wave_of(P + nb - 1), where
+// wave w owns [w S / G, (w+1) S / G); waves with an empty range wrote nothing.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
-                                                           const int* __restrict__ seqlens, uint16_t* __restrict__ O,
-                                                           float* __restrict__ LSE, int Hq, int Nmax, int nsplit) {
+__global__ __launch_bounds__(D) void decode_stream_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, const int* __restrict__ meta,
+    const int* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv,
+    int Nmax, int nht, int G) {
     const int hq = blockIdx.x, b = blockIdx.y;
     const int dcol = threadIdx.x;
+    const int g = Hq / Hkv, HK = Hkv * nht, TR = min(g, 32);
+    const int hk = hq / g, gh = hq % g, ht = gh / 32, hi = gh % 32;
     const int len = max(0, min(Nmax, seqlens[b]));
-    const int ns = (len + kDecodeSplit - 1) / kDecodeSplit;
-    const size_t row0 = (size_t)(b * Hq + hq) * nsplit;
+    const int nb = (len + 31) / 32;
     uint16_t* orow = O + (size_t)(b * Hq + hq) * D;
-    if (ns == 0) {
+    if (nb == 0) {
         orow[dcol] = 0;
         if (dcol == 0) LSE[b * Hq + hq] = kNegInf;
         return;
     }
+    const long long S = meta[B];
+    const int r = b * HK + hk * nht + ht;
+    const long long P = meta[b] + (long long)(hk * nht + ht) * nb;
+    auto wave_of = [&](long long st) { return (int)(((st + 1) * G - 1) / S); };
+    auto start_of = [&](int wv) { return (long long)wv * S / G; };
+    const int wf = wave_of(P), wl = wave_of(P + nb - 1);
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = __builtin_fmaxf(M, part_lse[row0 + s]);
+    for (int wv = wf; wv <= wl; ++wv)
+        if (start_of(wv) < start_of(wv + 1)) M = __builtin_fmaxf(M, part_lse[(size_t)(r + wv) * TR + hi]);
     float L = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = exp2_fast((part_lse[row0 + s] - M) * kLog2e);
-        L += w;
-        acc = __builtin_fmaf(w, part_o[(row0 + s) * D + dcol], acc);
+    for (int wv = wf; wv <= wl; ++wv) {
+        if (start_of(wv) == start_of(wv + 1)) continue;
+        const size_t slot = (size_t)(r + wv) * TR + hi;
+        const float wt = exp2_fast((part_lse[slot] - M) * kLog2e);
+        L += wt;
+        acc = __builtin_fmaf(wt, part_o[slot * D + dcol], acc);
     }
     orow[dcol] = f32_to_bf16_bits(acc / L);
     if (dcol == 0) LSE[b * Hq + hq] = M + log2_fast(L) * kLn2;
 }
 
-#ifndef DEC_RING
-#define DEC_RING 1
-#endif
 #ifndef DEC_STAGES
-#define DEC_STAGES 3
+#define DEC_STAGES 2
 #endif
 
 template <int D, int QR>
-static hipError_t launch_decode_ring(const DecodeArgs& a, int nht) {
-    using T = RingDecTile<D, DEC_STAGES, QR>;
-    auto kern = decode_ring_kernel<D, DEC_STAGES, QR>;
+static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
+    using T = StreamTile<D, DEC_STAGES, QR>;
+    auto kern = decode_stream_kernel<D, DEC_STAGES, QR>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.nsplit, a.Hkv * nht, a.B), dim3(64), T::LDS_BYTES, (hipStream_t)a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o,
-                       a.part_lse, a.Hq, a.Hkv, a.Nmax, a.nsplit, nht, a.scale * kLog2e);
-    return hipSuccess;
+    int dev = 0, ncu = 0, lds = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
+        return e;
+    // as many one-wave workgroups as the LDS of all CUs holds at once
+    const int per_cu = std::max(1, std::min(8, lds / T::LDS_BYTES));
+    const int G = std::max(1, std::min(kDecodeMaxWaves, ncu * per_cu));
+    hipLaunchKernelGGL(kern, dim3(G), dim3(64), T::LDS_BYTES, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o, a.part_lse, a.meta, a.B,
+                       a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_stream_combine_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, (hipStream_t)a.stream,
+                       a.part_o, a.part_lse, a.meta, a.seqlens, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nmax,
+                       nht, G);
+    return hipGetLastError();
 }
 
+// query rows staged in LDS: the group size rounded up to whole loads, at most 32
 template <int D>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     const int g = a.Hq / a.Hkv;
     const int nht = (g + 31) / 32;
-    hipError_t e;
-#if DEC_RING
-    {
-        // query rows staged in LDS: the group size rounded up to whole loads, at most 32
-        constexpr int RPL = 64 * 8 / D;   // rows per load instruction
-        const int rows = std::min(g, 32);
-        if (rows <= RPL) e = launch_decode_ring<D, RPL>(a, nht);
-        else if (rows <= 2 * RPL) e = launch_decode_ring<D, std::min(2 * RPL, 32)>(a, nht);
-        else if (rows <= 4 * RPL) e = launch_decode_ring<D, std::min(4 * RPL, 32)>(a, nht);
-        else e = launch_decode_ring<D, 32>(a, nht);
-        if (e != hipSuccess) return e;
-    }
-#else
-    {
-        using T = DecTile<D>;
-        auto kern = decode_split_kernel<D>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                T::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(a.nsplit, a.Hkv * nht, a.B), dim3(256), T::LDS_BYTES, (hipStream_t)a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o,
-                           a.part_lse, a.Hq, a.Hkv, a.Nmax, a.nsplit, nht, a.scale * kLog2e);
-    }
-#endif
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, (hipStream_t)a.stream, a.part_o,
-                       a.part_lse, a.seqlens, (uint16_t*)a.o, a.lse, a.Hq, a.Nmax, a.nsplit);
-    return hipGetLastError();
+    constexpr int RPL = 64 * 8 / D;   // rows per load instruction
+    const int rows = std::min(g, 32);
+    if (rows <= RPL) return launch_decode_stream<D, RPL>(a, nht);
+    if (rows <= 2 * RPL) return launch_decode_stream<D, std::min(2 * RPL, 32)>(a, nht);
+    if (rows <= 4 * RPL) return launch_decode_stream<D, std::min(4 * RPL, 32)>(a, nht);
+    return launch_decode_stream<D, 32>(a, nht);
+}
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d) {
+    (void)Nmax;
+    const int g = Hq / Hkv, nht = (g + 31) / 32, tr = std::min(g, 32);
+    const size_t slots = (size_t)B * Hkv * nht + kDecodeMaxWaves;
+    return slots * tr * (size_t)(d + 1) * sizeof(float) + ((size_t)B + 1) * sizeof(int);
+}
+
+void decode_workspace_layout(DecodeArgs& a, float* ws) {
+    const int g = a.Hq / a.Hkv, nht = (g + 31) / 32, tr = std::min(g, 32);
+    const size_t rows = ((size_t)a.B * a.Hkv * nht + kDecodeMaxWaves) * tr;
+    a.part_o = ws;
+    a.part_lse = ws + rows * a.d;
+    a.meta = reinterpret_cast<int*>(a.part_lse + rows);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a) {

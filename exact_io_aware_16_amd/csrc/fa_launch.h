@@ -46,9 +46,9 @@ struct DecodeArgs {
     float* lse;
     int B, Hq, Hkv, Nmax, d;
     float scale;
-    float* part_o;    // workspace: [B][Hq][nsplit][d] float32
-    float* part_lse;  // workspace: [B][Hq][nsplit] float32
-    int nsplit;
+    float* part_o;    // workspace: [slots][rows per slot][d] float32
+    float* part_lse;  // workspace: [slots][rows per slot] float32
+    int* meta;        // workspace: [B + 1] int32 (stage prefix per sequence)
     void* stream;
 };
 
@@ -58,7 +58,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 
-// Keys per decode split (one workgroup streams one split of one KV head).
-constexpr int kDecodeSplit = 512;
+// Workspace of the decode path: partial results for at most
+// (B * Hkv * ceil(g / 32) + kDecodeMaxWaves) slots of min(g, 32) rows each,
+// plus B + 1 stage-prefix integers.
+constexpr int kDecodeMaxWaves = 2048;
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d);
+// Points part_o, part_lse and meta of a into the workspace ws.
+void decode_workspace_layout(DecodeArgs& a, float* ws);
 
 }  // namespace fa

@@ -104,8 +104,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    fa_dtype_t dtype, float scale, int causal,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace fa_decode needs for its per-split partial results
- * (float32 partial outputs and logsumexps), linear in Nmax. */
+/* Bytes of device workspace fa_decode needs for its partial results (float32
+ * partial outputs and logsumexps of the pieces of each row that the streaming
+ * waves computed, plus B + 1 integers).  Independent of Nmax; 0 for shapes
+ * fa_decode would reject (Hq not a multiple of Hkv, non-positive sizes). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d);
 
 /*

@@ -46,16 +46,19 @@ def test_version_and_status_strings(lib):
     assert lib.fa_status_str(99).decode() == "unknown fa status"
 
 
-def test_workspaces_are_linear_in_sequence_length(lib):
+def test_workspace_sizes(lib):
     w1 = lib.fa_bwd_workspace_bytes(2, 16, 4096, 128)
     w2 = lib.fa_bwd_workspace_bytes(2, 16, 8192, 128)
     assert w1 == 2 * 16 * 4096 * 4 and w2 == 2 * w1
+    # decode partials do not grow with the cache length, only with the batch
     d1 = lib.fa_decode_workspace_bytes(16, 32, 8, 32768, 128)
     d2 = lib.fa_decode_workspace_bytes(16, 32, 8, 65536, 128)
-    assert d2 == 2 * d1
-    # far below one N x N score matrix
-    assert d1 < 16 * 32 * 32768 * 4
+    d3 = lib.fa_decode_workspace_bytes(32, 32, 8, 32768, 128)
+    assert d1 == d2 and d3 > d1
+    # far below the cache itself
+    assert d1 < 16 * 8 * 32768 * 128 * 2 // 64
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert lib.fa_decode_workspace_bytes(1, 3, 2, 64, 64) == 0   # Hq not a multiple of Hkv
 
 
 # Fake, 16-byte-aligned, never-dereferenced addresses: every call below fails

@@ -36,7 +36,25 @@ CASES = [
     (2, 64, 1, 600, 64, [600, 5]),             # 64 heads per group: two head tiles
     (2, 6, 6, 1500, 128, [1500, 1499]),        # g = 1
     (3, 4, 2, 900, 128, [0, 900, 17]),         # empty sequence -> O = 0, LSE = -inf
+    (2, 4, 2, 100, 128, [0, 0]),               # nothing to attend to anywhere
+    (1, 1, 1, 1, 64, [1]),                     # a single key
+    (2, 4, 1, 256, 128, [300, -5]),            # lengths clamped to [0, Nmax]
+    (1, 8, 1, 32768, 128, [32768]),            # one long row shared by every wave
 ]
+
+
+def test_decode_many_sequences_ragged():
+    """More sequences than one wave's 64 lanes, zero lengths among them: the
+    per-sequence stage counts are summed over several chunks of the batch."""
+    B, Hq, Hkv, Nmax, d = 70, 4, 2, 300, 64
+    lens = W.random_lengths(7, B, 0, Nmax)
+    lens[::9] = 0
+    w = W.random_case(70, B, Hq, Hkv, 1, Nmax, d)
+    announce(f"decode B70 ragged lengths {lens.tolist()}")
+    o, lse = run_decode(w.tensors["q"], w.tensors["k"], w.tensors["v"], lens, w.scale)
+    O, L = oracle.ref_decode(w.values("q"), w.values("k"), w.values("v"), lens, scale=w.scale)
+    assert_close("O", o, O, TOL_BF16)
+    assert_close("LSE", lse, L, TOL_BF16)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
