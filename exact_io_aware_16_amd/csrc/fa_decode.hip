@@ -162,14 +162,17 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
     // the same for a wave-uniform b (a scalar load)
     auto clen_u = [&](int b) { return max(0, min(Nmax, seqlens[__builtin_amdgcn_readfirstlane(b)])); };
 
-    // total stage count S; wave 0 records the exclusive prefix per sequence
-    int S = 0;
+    // total stage count S; wave 0 records the exclusive prefix per sequence.
+    // Lane l holds sequence b0 + l of the last chunk read (all of them when
+    // B <= 64, so the search below needs no second pass over the lengths).
+    int S = 0, len_l = 0, cnt_l = 0, incl_l = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int b = b0 + lane;
-        const int cnt = b < B ? (clen(b) + T::BK - 1) / T::BK * HK : 0;
-        const int incl = wave_incl_scan(cnt, lane);
-        if (w == 0 && b < B) meta[b] = S + incl - cnt;
-        S += __shfl(incl, 63, 64);
+        len_l = b < B ? clen(b) : 0;
+        cnt_l = (len_l + T::BK - 1) / T::BK * HK;
+        incl_l = wave_incl_scan(cnt_l, lane);
+        if (w == 0 && b < B) meta[b] = S + incl_l - cnt_l;
+        S += __shfl(incl_l, 63, 64);
     }
     S = __builtin_amdgcn_readfirstlane(S);
     if (w == 0 && lane == 0) meta[B] = S;
@@ -179,27 +182,31 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
     if (total <= 0) return;
 
     // the sequence holding stage s0, and s0's offset inside it
-    int b_st = 0, off = 0;
+    int b_st = 0, off = 0, len_st = 0;
     {
         int run = 0;
         for (int b0 = 0; b0 < B; b0 += 64) {
-            const int b = b0 + lane;
-            const int cnt = b < B ? (clen(b) + T::BK - 1) / T::BK * HK : 0;
-            const int incl = wave_incl_scan(cnt, lane);
-            const int excl = run + incl - cnt;
-            const unsigned long long m = __ballot(cnt > 0 && excl <= s0 && s0 < excl + cnt);
+            if (B > 64) {
+                const int b = b0 + lane;
+                len_l = b < B ? clen(b) : 0;
+                cnt_l = (len_l + T::BK - 1) / T::BK * HK;
+                incl_l = wave_incl_scan(cnt_l, lane);
+            }
+            const int excl = run + incl_l - cnt_l;
+            const unsigned long long m = __ballot(cnt_l > 0 && excl <= s0 && s0 < excl + cnt_l);
             if (m) {
                 const int l = __ffsll((long long)m) - 1;
                 b_st = b0 + l;
                 off = s0 - __shfl(excl, l, 64);
+                len_st = __shfl(len_l, l, 64);
                 break;
             }
-            run += __shfl(incl, 63, 64);
+            run += __shfl(incl_l, 63, 64);
         }
     }
     StreamCursor start;
     start.b = __builtin_amdgcn_readfirstlane(b_st);
-    start.len = clen_u(start.b);
+    start.len = __builtin_amdgcn_readfirstlane(len_st);
     start.nb = (start.len + T::BK - 1) / T::BK;
     off = __builtin_amdgcn_readfirstlane(off);
     start.ri = off / start.nb;
@@ -389,16 +396,37 @@ __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
     auto wave_of = [&](long long st) { return (int)(((st + 1) * G - 1) / S); };
     auto start_of = [&](int wv) { return (long long)wv * S / G; };
     const int wf = wave_of(P), wl = wave_of(P + nb - 1);
-    float M = kNegInf;
-    for (int wv = wf; wv <= wl; ++wv)
-        if (start_of(wv) < start_of(wv + 1)) M = __builtin_fmaxf(M, part_lse[(size_t)(r + wv) * TR + hi]);
-    float L = 0.f, acc = 0.f;
-    for (int wv = wf; wv <= wl; ++wv) {
-        if (start_of(wv) == start_of(wv + 1)) continue;
-        const size_t slot = (size_t)(r + wv) * TR + hi;
-        const float wt = exp2_fast((part_lse[slot] - M) * kLog2e);
-        L += wt;
-        acc = __builtin_fmaf(wt, part_o[slot * D + dcol], acc);
+    // The pieces' logsumexps are fetched together (one per thread) into LDS,
+    // a chunk at a time, and merged with a running maximum, so the loads of
+    // the pieces do not wait on each other.
+    constexpr int CH = 4 * D;
+    __shared__ float s_lse[CH];
+    float M = kNegInf, L = 0.f, acc = 0.f;
+    for (int c0 = wf; c0 <= wl; c0 += CH) {
+        const int nc = min(CH, wl - c0 + 1);
+        __syncthreads();
+        for (int t = dcol; t < nc; t += D) {
+            const int wv = c0 + t;
+            s_lse[t] = start_of(wv) < start_of(wv + 1) ? part_lse[(size_t)(r + wv) * TR + hi] : kNegInf;
+        }
+        __syncthreads();
+        float cm = kNegInf;
+        for (int t = 0; t < nc; ++t) cm = __builtin_fmaxf(cm, s_lse[t]);
+        const float m_new = __builtin_fmaxf(M, cm);
+        const float corr = M == kNegInf ? 0.f : exp2_fast((M - m_new) * kLog2e);
+        L *= corr;
+        acc *= corr;
+        M = m_new;
+#pragma unroll 4
+        for (int t = 0; t < nc; ++t) {
+            // a wave with no stages wrote nothing: weight 0, and its slot's
+            // (unwritten) contents are discarded by the select
+            const float l = s_lse[t];
+            const float v = part_o[((size_t)(r + c0 + t) * TR + hi) * D + dcol];
+            const float wt = exp2_fast((l - M) * kLog2e);
+            L += wt;
+            acc += l == kNegInf ? 0.f : wt * v;
+        }
     }
     orow[dcol] = f32_to_bf16_bits(acc / L);
     if (dcol == 0) LSE[b * Hq + hq] = M + log2_fast(L) * kLn2;
