@@ -61,7 +61,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d) {
     (void)d;
     if (B < 1 || Hq < 1 || Nq < 1) return 0;
-    return (size_t)B * Hq * Nq * sizeof(float);
+    return 2 * (size_t)B * Hq * Nq * sizeof(float);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

@@ -29,6 +29,8 @@
 
 namespace fa {
 
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 namespace {
 
 // Row strides of the LDS tiles: RS for 16-byte row reads (each 16-lane group
@@ -51,10 +53,13 @@ __device__ __forceinline__ void store_grad4(uint16_t* dst, float a, float b, flo
 // ---------------------------------------------------------------------------
 // 1. D_i = dO_i . O_i
 // ---------------------------------------------------------------------------
+// Also writes lse2_i = lse_i log2(e) (+inf for rows that saw no key, so that
+// P = exp2(s scale log2 e - lse2) = 0 there), the form the dK/dV kernel streams.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const uint16_t* __restrict__ O,
                                                              const uint16_t* __restrict__ dO,
-                                                             float* __restrict__ delta, int rows) {
+                                                             const float* __restrict__ LSE, float* __restrict__ delta,
+                                                             float* __restrict__ lse2, int rows) {
     constexpr int LPR = D / 8;  // lanes per row
     const int t = blockIdx.x * 256 + threadIdx.x;
     const int row = t / LPR, c8 = t % LPR;
@@ -70,7 +75,11 @@ __global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const uint16_t* __r
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && c8 == 0) delta[row] = acc;
+    if (row < rows && c8 == 0) {
+        delta[row] = acc;
+        const float l = LSE[row];
+        lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int bh = id % BH;
     const int b = bh / Hq, h = bh % Hq;
     const int hk = h / (Hq / Hkv);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, hf = lane >> 5;
     const int off = Nk - Nq;
     const int qw = qb * T::BM + wave * 32;
@@ -210,19 +219,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkvTile {
-    static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
-    static constexpr int BQ = 32;        // queries per block
-    static constexpr int RS = Strides<D>::RS, TS = Strides<D>::TS;
-    static constexpr int NAT = BQ * RS, TR = BQ * TS;
-    static constexpr int STAGE = 2 * NAT + 2 * TR + 2 * BQ * 2;  // + lse2 and delta (float = 2 elems)
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int CPT = BQ * D / 8 / 256;   // 16-byte chunks per thread per tensor
+    static constexpr int BK = 128;                 // keys per workgroup (4 waves x 32)
+    static constexpr int BQ = 32;                  // queries per step
+    static constexpr int TILE = BQ * D;            // elements of one Q (or dO) tile
+    static constexpr int AUX = 2 * BQ;             // floats per step: lse2[BQ], then delta[BQ]
+    static constexpr int STAGE = 2 * TILE + 2 * AUX;   // uint16 elements
+    static constexpr int NS = 3;                   // ring stages
+    static constexpr int LDS_BYTES = NS * STAGE * 2;
+    static constexpr int IPW = TILE / 8 / 64 / 4;  // 16-byte load instructions per wave per tile
+    static constexpr int LPS = 2 * IPW + 1;        // per wave per stage (Q, dO, lse2/delta)
+    static_assert(IPW >= 1 && TILE / 8 == IPW * 256, "tile must split evenly over the waves");
+    static_assert((NS - 2) * LPS < 64, "vmcnt range");
 };
 
+// Key owner.  Q and dO tiles (BQ query rows each, dense and XOR-swizzled so
+// that both 16-byte row reads and transposing reads are conflict-free) and
+// the rows' lse2 and D travel global -> LDS with direct-to-LDS loads into a
+// ring of NS stages, NS-1 steps ahead; one barrier per step.
 template <int D, bool CAUSAL, typename G>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
     G* __restrict__ dK, G* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkb, float sl2, float scale) {
     using T = DkvTile<D>;
     extern __shared__ __align__(16) uint16_t smem[];
@@ -232,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int bhk = id / nkb;
     const int b = bhk / Hkv, hk = bhk % Hkv;
     const int g = Hq / Hkv;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, hf = lane >> 5;
     const int off = Nk - Nq;
     const int kw = kblk * T::BK + wave * 32;   // first key of this wave
@@ -240,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int kc = min(kj, Nk - 1);
     const size_t krow = (size_t)(b * Hkv + hk) * Nk + kc;
 
+    // K^T and V^T as the B operands: lane (n, hf) holds key kw + n
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -261,105 +279,114 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int total = g * nqblk;   // (head, query block) steps
     const int wave_q_begin = CAUSAL ? max(0, kw - off) : 0;
 
-    // Q and dO are each staged twice: row-read stride (S = Q K^T, dP = dO V^T)
-    // and transpose-read stride (dK^T += Q^T dS, dV^T += dO^T P).  Threads
-    // 0 .. 2*BQ-1 also fetch lse*log2(e) (rows past Nq or with no visible key
-    // get +inf, i.e. P = 0) and D.
-    u32x4 qr[T::CPT], dr[T::CPT];
-    float aux = 0.f;
-    auto load = [&](int step) {
+    // step -> (query head, first query row)
+    auto step_rows = [&](int step, size_t& base, int& q0) {
         const int hq = hk * g + step / nqblk;
-        const int q0 = (qb0 + step % nqblk) * T::BQ;
-        const size_t base = (size_t)(b * Hq + hq) * Nq;
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), c8 = c % (D / 8);
-            const size_t gi = (base + min(q0 + row, Nq - 1)) * D + c8 * 8;
-            qr[r] = *reinterpret_cast<const u32x4*>(Q + gi);
-            dr[r] = *reinterpret_cast<const u32x4*>(dO + gi);
-        }
-        if (tid < 2 * T::BQ) {
-            const int qrow = min(q0 + (tid % T::BQ), Nq - 1);
-            if (tid < T::BQ) {
-                const float l = LSE[base + qrow];
-                aux = (q0 + tid < Nq && l != kNegInf) ? l * kLog2e : __builtin_huge_valf();
-            } else {
-                aux = delta[base + qrow];
-            }
-        }
+        q0 = (qb0 + step % nqblk) * T::BQ;
+        base = (size_t)(b * Hq + hq) * Nq;
     };
-    auto store = [&](uint16_t* st) {
+    // this wave's share of step `step` into ring slot `slot` (steps past the
+    // end reload the last one, rows past Nq reload row Nq - 1: the number of
+    // loads per step is fixed and every address is valid)
+    auto issue = [&](int step, int slot) {
+        size_t base;
+        int q0;
+        step_rows(min(step, total - 1), base, q0);
+        uint16_t* tq = smem + slot * T::STAGE;
+        uint16_t* tdo = tq + T::TILE;
+        uint16_t* taux = tdo + T::TILE;
 #pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), c8 = c % (D / 8);
-            *reinterpret_cast<u32x4*>(st + row * T::RS + c8 * 8) = qr[r];
-            *reinterpret_cast<u32x4*>(st + T::NAT + row * T::RS + c8 * 8) = dr[r];
-            *reinterpret_cast<u32x4*>(st + 2 * T::NAT + row * T::TS + c8 * 8) = qr[r];
-            *reinterpret_cast<u32x4*>(st + 2 * T::NAT + T::TR + row * T::TS + c8 * 8) = dr[r];
+        for (int i = 0; i < T::IPW; ++i) {
+            const int sl = (wave * T::IPW + i) * 64 + lane;
+            const int row = sl / (D / 8), pos = sl % (D / 8);
+            const size_t gi = (base + min(q0 + row, Nq - 1)) * D + ((pos ^ swz<D>(row)) << 3);
+            const int lds_off = (wave * T::IPW + i) * 64 * 8;
+            __builtin_amdgcn_global_load_lds(Q + gi, LDS_PTR(tq + lds_off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dO + gi, LDS_PTR(tdo + lds_off), 16, 0, 0);
         }
-        if (tid < 2 * T::BQ) reinterpret_cast<float*>(st + 2 * T::NAT + 2 * T::TR)[tid] = aux;
+        // lanes 0..BQ-1: lse2 of the step's rows, lanes BQ..2BQ-1: D (every
+        // wave writes the same 256 bytes, which keeps the per-wave count equal)
+        const int r = min(q0 + (lane % T::BQ), Nq - 1);
+        const float* src = lane < T::BQ ? lse2 + base + r : delta + base + r;
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(taux), 4, 0, 0);
     };
 
     if (total > 0) {
-        load(0);
-        store(smem);
-    }
-    __syncthreads();
-    for (int stp = 0; stp < total; ++stp) {
-        const int q0 = (qb0 + stp % nqblk) * T::BQ;
-        uint16_t* st = smem + (stp & 1) * T::STAGE;
-        if (stp + 1 < total) load(stp + 1);
-        if (q0 + T::BQ > wave_q_begin && kw < Nk) {
-            const uint16_t* sQ = st;
-            const uint16_t* sdO = st + T::NAT;
-            const uint16_t* sQT = st + 2 * T::NAT;
-            const uint16_t* sdOT = sQT + T::TR;
-            const float* sL = reinterpret_cast<const float*>(sdOT + T::TR);
-            const float* sD = sL + T::BQ;
-            f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                s = mfma32x32x16(frag_rows(sQ, T::RS, 0, kk * 16, lane), kf[kk], s);
-                dp = mfma32x32x16(frag_rows(sdO, T::RS, 0, kk * 16, lane), vf[kk], dp);
+        for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
+    }
+    for (int stp = 0; stp < total; ++stp) {
+        const int slot = stp % T::NS;
+        // this wave's loads of step stp are done once at most NS-2 younger stages remain
+        wait_vmcnt<(T::NS - 2) * T::LPS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(stp + T::NS - 1, (stp + T::NS - 1) % T::NS);
+        size_t base_unused;
+        int q0;
+        step_rows(stp, base_unused, q0);
+        if (q0 + T::BQ > wave_q_begin && kw < Nk) {
+            const uint16_t* sQ = smem + slot * T::STAGE;
+            const uint16_t* sdO = sQ + T::TILE;
+            const float* sL = reinterpret_cast<const float*>(sdO + T::TILE);
+            const float* sD = sL + T::BQ;
+            // S = Q K^T, dP = dO V^T: one key per lane, 16 query rows per lane
+            // fragments are read four k-steps at a time, ahead of their MFMAs
+            f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+            for (int k0 = 0; k0 < D / 16; k0 += 4) {
+                bf16x8 qa[4], da[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    qa[kk] = frag_rows_swz<D>(sQ, 0, (k0 + kk) * 16, lane);
+                    da[kk] = frag_rows_swz<D>(sdO, 0, (k0 + kk) * 16, lane);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    sc = mfma32x32x16(qa[kk], kf[k0 + kk], sc);
+                    dp = mfma32x32x16(da[kk], vf[k0 + kk], dp);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 fragment reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
             }
-            const bool need_mask = kw + 32 > Nk || (CAUSAL && kw + 31 > q0 + off);
+            const bool need_mask = kw + 32 > Nk || q0 + T::BQ > Nq || (CAUSAL && kw + 31 > q0 + off);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int r0 = gq * 8 + hf * 4;   // query rows r0..r0+3 of this block
+                const int r0 = gq * 8 + hf * 4;   // query rows r0..r0+3 of this step
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + r0);
                 const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = gq * 4 + r;
-                    float p = exp2_fast(__builtin_fmaf(s[i], sl2, -l4[r]));
+                    float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -l4[r]));
                     if (need_mask) {
-                        const bool ok = kj < Nk && (!CAUSAL || kj <= q0 + r0 + r + off);
+                        const int qi = q0 + r0 + r;
+                        const bool ok = kj < Nk && qi < Nq && (!CAUSAL || kj <= qi + off);
                         p = ok ? p : 0.f;
                     }
-                    s[i] = p;
+                    sc[i] = p;
                     dp[i] = p * (dp[i] - d4[r]);   // dS
                 }
             }
+            // dV^T += dO^T P and dK^T += Q^T dS, transposing reads of the same tiles
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 pb, db;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    pb[e] = (__bf16)s[ks * 8 + e];
+                    pb[e] = (__bf16)sc[ks * 8 + e];
                     db[e] = (__bf16)dp[ks * 8 + e];
                 }
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md) {
-                    dv[md] = mfma32x32x16(frag_tr(sdOT, T::TS, ks * 16, md * 32, lane), pb, dv[md]);
-                    dk[md] = mfma32x32x16(frag_tr(sQT, T::TS, ks * 16, md * 32, lane), db, dk[md]);
+                    dv[md] = mfma32x32x16(frag_tr_swz<D>(sdO, ks * 16, md * 32, lane), pb, dv[md]);
+                    dk[md] = mfma32x32x16(frag_tr_swz<D>(sQ, ks * 16, md * 32, lane), db, dk[md]);
                 }
             }
         }
-        if (stp + 1 < total) store(smem + ((stp + 1) & 1) * T::STAGE);
-        __syncthreads();
     }
+    // the trailing look-ahead loads must land before the workgroup exits
+    wait_vmcnt<0>();
     if (kj < Nk) {
         const size_t o = ((size_t)(b * Hkv + hk) * Nk + kj) * D;
 #pragma unroll
@@ -541,8 +568,9 @@ template <int D, bool CAUSAL, typename G>
 static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
     const hipStream_t s = (hipStream_t)a.stream;
     const int rows = a.B * a.Hq * a.Nq;
+    float* lse2 = a.delta + rows;
     hipLaunchKernelGGL(bwd_delta_bf16_kernel<D>, dim3((rows * (D / 8) + 255) / 256), dim3(256), 0, s,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dO, a.delta, rows);
+                       (const uint16_t*)a.o, (const uint16_t*)a.dO, a.lse, a.delta, lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float sl2 = a.scale * kLog2e;
@@ -568,7 +596,7 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
                                 T::LDS_BYTES);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(nkb * a.B * a.Hkv), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, lse2, a.delta,
                            (G*)a.dk, (G*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, nkb, sl2, a.scale);
     }
     return hipGetLastError();

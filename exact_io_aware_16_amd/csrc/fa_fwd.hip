@@ -660,7 +660,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
     using T = RingTile<D, NW, S, NT>;
     const int hk = h / (Hq / Hkv);
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, hf = lane >> 5;
 
     const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;

@@ -33,7 +33,7 @@ struct BwdArgs {
     int B, Hq, Hkv, Nq, Nk, d;
     float scale;
     int causal;
-    float* delta;  // workspace: [B][Hq][Nq] float32
+    float* delta;  // workspace: [2][B][Hq][Nq] float32 (D, then lse log2 e for bf16 inputs)
     void* stream;
 };
 

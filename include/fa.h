@@ -85,8 +85,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int Hq, int Hkv, int Nq, int Nk, int d,
                    fa_dtype_t dtype, float scale, int causal, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: one float32 per query row
- * (D_i = dO_i . O_i), i.e. linear in Nq, never Nq x Nk. */
+/* Bytes of device workspace fa_bwd needs: two float32 per query row
+ * (D_i = dO_i . O_i and lse_i log2 e), i.e. linear in Nq, never Nq x Nk. */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
 
 /*

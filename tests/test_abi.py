@@ -49,7 +49,7 @@ def test_version_and_status_strings(lib):
 def test_workspace_sizes(lib):
     w1 = lib.fa_bwd_workspace_bytes(2, 16, 4096, 128)
     w2 = lib.fa_bwd_workspace_bytes(2, 16, 8192, 128)
-    assert w1 == 2 * 16 * 4096 * 4 and w2 == 2 * w1
+    assert w1 == 2 * (2 * 16 * 4096 * 4) and w2 == 2 * w1
     # decode partials do not grow with the cache length, only with the batch
     d1 = lib.fa_decode_workspace_bytes(16, 32, 8, 32768, 128)
     d2 = lib.fa_decode_workspace_bytes(16, 32, 8, 65536, 128)
