@@ -14,13 +14,15 @@
 //  2. bwd_dq (query owner, shaped like the forward pass): each wave owns 32
 //     query rows; S^T = K Q^T and dP^T = V dO^T put one query per lane, so
 //     lse_i and D_i are per-lane scalars; dQ^T += K^T dS^T accumulates in
-//     registers (K is staged twice in LDS: as is, and transposed + key-permuted
-//     so a lane's eight keys are contiguous).
+//     registers.  K and V blocks stream through a ring of LDS stages filled
+//     by direct-to-LDS loads; K is read both row-wise and with transposing
+//     reads (ds_read_b64_tr_b16) from the same XOR-swizzled tile.
 //  3. bwd_dkdv (key owner): each wave owns 32 keys for the whole pass, K and V
 //     rows sit in registers, and for every query head of the group and every
 //     query block S = Q K^T and dP = dO V^T put one key per lane; then
-//     dV^T += dO^T P and dK^T += Q^T dS accumulate in registers (Q and dO are
-//     staged as is and transposed).  Grouped heads are summed in registers.
+//     dV^T += dO^T P and dK^T += Q^T dS accumulate in registers.  Q and dO
+//     tiles and the rows' lse log2 e and D stream through an LDS ring the
+//     same way.  Grouped heads are summed in registers.
 // The key-owner kernel recomputes S and dP that the query-owner kernel also
 // computes (7 matrix products instead of 5); that buys determinism and removes
 // every atomic read-modify-write of dQ.
@@ -32,14 +34,6 @@ namespace fa {
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 namespace {
-
-// Row strides of the LDS tiles: RS for 16-byte row reads (each 16-lane group
-// hits 16 distinct bank quads), TS (64 B mod 256 B) for the transposing reads.
-template <int D>
-struct Strides {
-    static constexpr int RS = D + 8;
-    static constexpr int TS = D + 32;
-};
 
 __device__ __forceinline__ void store_grad4(float* dst, float a, float b, float c, float d) {
     *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
@@ -87,13 +81,16 @@ __global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTile {
-    static constexpr int BM = 128;       // queries per workgroup (4 waves x 32)
-    static constexpr int BN = 32;        // keys per block
-    static constexpr int RS = Strides<D>::RS, TS = Strides<D>::TS;
-    static constexpr int K_EL = BN * RS, KT_EL = BN * TS, V_EL = BN * RS;
-    static constexpr int STAGE = K_EL + KT_EL + V_EL;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int CPT = BN * D / 8 / 256;   // 16-byte chunks per thread per tensor
+    static constexpr int BM = 128;                 // queries per workgroup (4 waves x 32)
+    static constexpr int BN = 32;                  // keys per block
+    static constexpr int TILE = BN * D;            // elements of one K (or V) block
+    static constexpr int STAGE = 2 * TILE;         // K then V
+    static constexpr int NS = 3;                   // ring stages
+    static constexpr int LDS_BYTES = NS * STAGE * 2;
+    static constexpr int IPW = TILE / 8 / 64 / 4;  // 16-byte load instructions per wave per tile
+    static constexpr int LPS = 2 * IPW;
+    static_assert(IPW >= 1 && TILE / 8 == IPW * 256, "tile must split evenly over the waves");
+    static_assert((NS - 2) * LPS < 64, "vmcnt range");
 };
 
 template <int D, bool CAUSAL, typename G>
@@ -138,46 +135,53 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) acc[md] = zero16();
 
-    // K is staged twice (row-read stride for S^T = K Q^T, transpose-read stride
-    // for dQ^T = K^T dS^T); V once.  Rows at or past kv_end read row kv_end - 1.
-    u32x4 kr[T::CPT], vr[T::CPT];
-    auto load = [&](int key0) {
+    // K and V blocks (dense, XOR-swizzled) travel global -> LDS with
+    // direct-to-LDS loads into a ring of NS stages, NS-1 blocks ahead; K is
+    // read row-wise for S^T = K Q^T and with transposing reads for
+    // dQ^T += K^T dS^T.  Rows at or past kv_end read row kv_end - 1.
+    auto issue = [&](int blk, int slot) {
+        uint16_t* kt = smem + slot * T::STAGE;
+        uint16_t* vt = kt + T::TILE;
 #pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), c8 = c % (D / 8);
-            const size_t gi = (size_t)min(key0 + row, kv_end - 1) * D + c8 * 8;
-            kr[r] = *reinterpret_cast<const u32x4*>(kb + gi);
-            vr[r] = *reinterpret_cast<const u32x4*>(vb + gi);
-        }
-    };
-    auto store = [&](uint16_t* st) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), c8 = c % (D / 8);
-            *reinterpret_cast<u32x4*>(st + row * T::RS + c8 * 8) = kr[r];
-            *reinterpret_cast<u32x4*>(st + T::K_EL + row * T::TS + c8 * 8) = kr[r];
-            *reinterpret_cast<u32x4*>(st + T::K_EL + T::KT_EL + row * T::RS + c8 * 8) = vr[r];
+        for (int i = 0; i < T::IPW; ++i) {
+            const int sl = (wave * T::IPW + i) * 64 + lane;
+            const int row = sl / (D / 8), pos = sl % (D / 8);
+            const size_t gi = (size_t)min(blk * T::BN + row, kv_end - 1) * D + ((pos ^ swz<D>(row)) << 3);
+            const int lds_off = (wave * T::IPW + i) * 64 * 8;
+            __builtin_amdgcn_global_load_lds(kb + gi, LDS_PTR(kt + lds_off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + gi, LDS_PTR(vt + lds_off), 16, 0, 0);
         }
     };
 
-    load(0);
-    store(smem);
-    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
     for (int j = 0; j < nblk; ++j) {
         const int key0 = j * T::BN;
-        uint16_t* st = smem + (j & 1) * T::STAGE;
-        if (j + 1 < nblk) load(key0 + T::BN);
+        const int slot = j % T::NS;
+        // this wave's loads of block j are done once at most NS-2 younger stages remain
+        wait_vmcnt<(T::NS - 2) * T::LPS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + T::NS - 1, (j + T::NS - 1) % T::NS);
         if (key0 < wave_end) {
-            const uint16_t* sK = st;
-            const uint16_t* sKT = st + T::K_EL;
-            const uint16_t* sV = st + T::K_EL + T::KT_EL;
+            const uint16_t* sK = smem + slot * T::STAGE;
+            const uint16_t* sV = sK + T::TILE;
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                s = mfma32x32x16(frag_rows(sK, T::RS, 0, kk * 16, lane), qf[kk], s);
-                dp = mfma32x32x16(frag_rows(sV, T::RS, 0, kk * 16, lane), df[kk], dp);
+            for (int k0 = 0; k0 < D / 16; k0 += 4) {
+                bf16x8 ka[4], va[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    ka[kk] = frag_rows_swz<D>(sK, 0, (k0 + kk) * 16, lane);
+                    va[kk] = frag_rows_swz<D>(sV, 0, (k0 + kk) * 16, lane);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    s = mfma32x32x16(ka[kk], qf[k0 + kk], s);
+                    dp = mfma32x32x16(va[kk], df[k0 + kk], dp);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 fragment reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
             }
             const bool need_mask = key0 + T::BN > kv_end || (CAUSAL && key0 + T::BN > qw + off);
 #pragma unroll
@@ -197,12 +201,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 for (int e = 0; e < 8; ++e) db[e] = (__bf16)s[ks * 8 + e];
 #pragma unroll
                 for (int md = 0; md < D / 32; ++md)
-                    acc[md] = mfma32x32x16(frag_tr(sKT, T::TS, ks * 16, md * 32, lane), db, acc[md]);
+                    acc[md] = mfma32x32x16(frag_tr_swz<D>(sK, ks * 16, md * 32, lane), db, acc[md]);
             }
         }
-        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * T::STAGE);
-        __syncthreads();
     }
+    // the trailing look-ahead loads must land before the workgroup exits
+    wait_vmcnt<0>();
     if (qi < Nq) {
         G* out = dQ + ((size_t)(b * Hq + h) * Nq + qi) * D;
 #pragma unroll
