@@ -86,35 +86,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // Wave-uniform "all lanes true".
 __device__ __forceinline__ bool wave_all(bool p) { return __all(p); }
 
-// ---------------------------------------------------------------------------
-// Matrix-core operand fragments read from LDS tiles stored row-major
-// (row = key or query, d contiguous).
-// ---------------------------------------------------------------------------
-
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// A (or B) fragment of X itself: lane l gets X[r0 + l%32][c0 + 8*(l/32) .. +7]
-// (one 16-byte read).
-__device__ __forceinline__ bf16x8 frag_rows(const uint16_t* X, int S, int r0, int c0, int lane) {
-    return *reinterpret_cast<const bf16x8*>(X + (r0 + (lane & 31)) * S + c0 + (lane >> 5) * 8);
-}
-
-// A fragment of X^T (rows of the fragment = columns of X, k = rows of X) from
-// the same row-major tile, with two ds_read_b64_tr_b16: lane l gets
-// X[k0 + 8*(e/4) + 4*(l/32) + e%4][c0 + l%32] for e = 0..7.
-// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
-// 8-byte chunks addressed by lanes 4j + i/4 (j = 0..3), i.e. it transposes a
-// 4-row x 16-column block; each lane therefore addresses row k0 + 4*(l/32) +
-// (l%16)/4 at column c0 + 16*((l/16)%2) + 4*(l%4).
-__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* X, int S, int k0, int c0, int lane) {
-    const int t = lane & 15;
-    const int row = k0 + (lane >> 5) * 4 + (t >> 2);
-    const int col = c0 + ((lane >> 4) & 1) * 16 + (t & 3) * 4;
-    const uint16_t* p = X + row * S + col;
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * S));
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // ---------------------------------------------------------------------------
 // Dense LDS tiles written by direct-to-LDS loads (no padding possible: each
@@ -137,13 +109,25 @@ __device__ __forceinline__ int swz_off(int r, int c) {
     return r * D + ((c ^ swz<D>(r)) << 3);
 }
 
-// frag_rows on a swizzled dense tile [rows][D]
+// ---------------------------------------------------------------------------
+// Matrix-core operand fragments read from those tiles (row = key or query,
+// d contiguous).
+// ---------------------------------------------------------------------------
+
+// A (or B) fragment of X itself: lane l gets X[r0 + l%32][c0 + 8*(l/32) .. +7]
+// (one 16-byte read).
 template <int D>
 __device__ __forceinline__ bf16x8 frag_rows_swz(const uint16_t* X, int r0, int c0, int lane) {
     return *reinterpret_cast<const bf16x8*>(X + swz_off<D>(r0 + (lane & 31), (c0 >> 3) + (lane >> 5)));
 }
 
-// frag_tr on a swizzled dense tile [rows][D] (same lane mapping as frag_tr)
+// A fragment of X^T (rows of the fragment = columns of X, k = rows of X) from
+// the same tile, with two ds_read_b64_tr_b16: lane l gets
+// X[k0 + 8*(e/4) + 4*(l/32) + e%4][c0 + l%32] for e = 0..7.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
+// 8-byte chunks addressed by lanes 4j + i/4 (j = 0..3), i.e. it transposes a
+// 4-row x 16-column block; each lane therefore addresses row k0 + 4*(l/32) +
+// (l%16)/4 at column c0 + 16*((l/16)%2) + 4*(l%4).
 template <int D>
 __device__ __forceinline__ bf16x8 frag_tr_swz(const uint16_t* X, int k0, int c0, int lane) {
     const int t = lane & 15;
@@ -173,12 +157,5 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-
-// Column E (0..7) of two 8 x bf16 row chunks, packed as (row a, row b) in one
-// dword: low half from a, high half from b (one v_perm_b32).
-template <int E>
-__device__ __forceinline__ uint32_t pack_col(const u32x4& a, const u32x4& b) {
-    return __builtin_amdgcn_perm(b[E >> 1], a[E >> 1], (E & 1) ? 0x07060302u : 0x05040100u);
-}
 
 }  // namespace fa

@@ -8,74 +8,65 @@
 // exp(scores - m) and its product with V; divide by l once at the end.  The
 // N x N score matrix only ever exists one register tile at a time.
 //
-// MI355X mapping (bf16 kernel):
-//  * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//    owns 32 query rows for the whole pass;
-//  * K/V blocks of 64 keys are staged through LDS, double buffered, with the
-//    next block's global loads in flight while the current block is computed;
+// MI355X mapping (bf16 kernel, fwd_ring_kernel):
+//  * one workgroup = NW waves of 32 query rows of one (batch, head); each wave
+//    owns its rows for the whole pass;
+//  * K/V blocks of 64 keys go global -> LDS with direct-to-LDS loads
+//    (global_load_lds_dwordx4) into a ring of S stages, S-1 blocks ahead, into
+//    dense tiles with an XOR swizzle that keeps both row reads and transposing
+//    reads (ds_read_b64_tr_b16) free of bank conflicts;
 //  * scores are computed transposed, S^T = K Q^T (32x32x16 bf16 MFMA, fp32
 //    accumulate), so every lane owns one query column: the row max and row sum
 //    are per-lane reductions plus one exchange with lane l^32;
-//  * the output is accumulated transposed too, O^T += V^T P^T, so the rescale
-//    by exp(m_old - m_new) is a per-lane scalar; V is written to LDS already
-//    transposed (and key-permuted so each lane's eight keys are contiguous);
-//  * the softmax runs in base 2 with scale*log2(e) folded into one FMA;
+//  * the output is accumulated transposed too, O^T += V^T P^T, with V^T read
+//    straight from the row-major V tile by transposing LDS reads, so the
+//    rescale by exp(m_old - m_new) is a per-lane scalar;
+//  * the softmax runs in base 2 with scale*log2(e) folded into one FMA, and the
+//    running max is raised lazily;
 //  * causal: key blocks past the workgroup's last visible key are never
 //    loaded, blocks past a wave's last visible key are skipped by that wave,
 //    and only blocks crossing the diagonal pay for the mask;
 //  * workgroups are issued heaviest query block first, and the blocks of one
-//    (batch, head) are a multiple of 8 launch slots apart, so they land on the
-//    same XCD and share its L2 copy of K and V.
+//    (batch, head) are BH launch slots apart, so with BH a multiple of 8 they
+//    land on the same XCD and share its L2 copy of K and V.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 #include <algorithm>
 
-// Query column tiles per wave for each head dimension.
-#ifndef FWD_NT64
-#define FWD_NT64 1
-#endif
-#ifndef FWD_NT128
-#define FWD_NT128 1
-#endif
-// Causal: pair query blocks (p, nqb-1-p) in one workgroup (1) or issue single
-// blocks heaviest first (0).
-#ifndef FWD_PAIR
-#define FWD_PAIR 0
-#endif
-// Software-pipelined block loop (1) or the plain one (0).
-#ifndef FWD_PIPE
-#define FWD_PIPE 1
-#endif
-// Direct-to-LDS ring kernel (1) or the register-staged kernels (0), and its
-// waves per workgroup / ring stages per head dimension.
-#ifndef FWD_RING
-#define FWD_RING 1
-#endif
 #ifndef RING_NW64
-#define RING_NW64 4
+#define RING_NW64 4      // waves per workgroup, d = 64
 #endif
 #ifndef RING_S64
-#define RING_S64 2
+#define RING_S64 2       // ring stages, d = 64
 #endif
 #ifndef RING_NW128
-#define RING_NW128 8
+#define RING_NW128 8     // waves per workgroup, d = 128
 #endif
 #ifndef RING_S128
-#define RING_S128 4
+#define RING_S128 4      // ring stages, d = 128
 #endif
 #ifndef RING_NT64
-#define RING_NT64 1
+#define RING_NT64 1      // 32-query column tiles per wave, d = 64
 #endif
-// key groups (of 16) whose V fragments are fetched before the exponentials (d = 64)
+#ifndef RING_NT128
+#define RING_NT128 1     // 32-query column tiles per wave, d = 128
+#endif
+// V fragments requested before the exponentials (d = 64, NT = 1)
 #ifndef RING_VH64
 #define RING_VH64 4
 #endif
-// ring kernel: order the S = K Q^T fragment reads ahead of their MFMAs
+// order the S = K Q^T fragment reads ahead of their MFMAs
 #ifndef RING_SGB
 #define RING_SGB 1
 #endif
-// software-pipelined kernel (FWD_SP), its waves per workgroup and minimum waves per SIMD
+// minimum waves per SIMD the d = 64 ring kernel is compiled for (caps its VGPRs)
+#ifndef RING_WPE64
+#define RING_WPE64 2
+#endif
+// Software-pipelined kernel (fwd_sp_kernel) instead of the ring kernel: its
+// waves per workgroup and minimum waves per SIMD; SP_PIN keeps each chunk of
+// exponentials next to its MFMA; SP_PAIR pairs causal query blocks.
 #ifndef FWD_SP
 #define FWD_SP 0
 #endif
@@ -94,535 +85,14 @@
 #ifndef SP_PAIR
 #define SP_PAIR 1
 #endif
-// minimum waves per SIMD the d=64 ring kernel is compiled for (caps its VGPRs)
-#ifndef RING_WPE64
-#define RING_WPE64 2
-#endif
-#ifndef RING_NT128
-#define RING_NT128 1
-#endif
-// Explicit instruction schedule of the pipelined loop's overlap region.
-#ifndef FWD_SCHED
-#define FWD_SCHED 1
-#endif
-#if FWD_PIPE
-#define FWD_QBLOCK fwd_qblock_pipe
-#else
-#define FWD_QBLOCK fwd_qblock
-#endif
-// Row sums with v_dot2c_f32_bf16 on the packed bf16 P (1) or float adds (0).
-#ifndef FWD_DOT2
-#define FWD_DOT2 0
-#endif
 
 namespace fa {
-
-template <int D, int NT>
-struct FwdTile {
-    static constexpr int NW = 4;               // waves per workgroup
-    static constexpr int QW = 32 * NT;         // query rows per wave (NT column tiles of 32)
-    static constexpr int BM = NW * QW;         // query rows per workgroup
-    static constexpr int BN = 64;              // keys per K/V block
-    static constexpr int KS = D + 8;           // K row stride: 16-lane row reads hit 16 distinct bank quads
-    static constexpr int VS = D + 32;          // V row stride (64 B mod 256 B): transpose reads 2-way at most
-    static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = BN * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int CH = BN * D / 8;      // 16-byte chunks per K (or V) block
-    static constexpr int CPT = CH / 256;       // chunks per thread
-};
 
 // Lazy rescaling threshold (log2 units): the running max is only raised when
 // some row's block max exceeds it by more than 2^8; until then probabilities
 // up to 2^8 are accumulated against the stale max.  O and l share that max, so
 // the final O / l is unchanged (exact up to rounding).
 constexpr float kRescaleThreshold = 8.0f;
-
-// One query block of one (batch, head): the whole online-softmax pass.
-template <int D, int NT, bool CAUSAL>
-__device__ __forceinline__ void fwd_qblock(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                           float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b, int h,
-                                           int qb, float sl2, uint16_t* smem) {
-    using T = FwdTile<D, NT>;
-    const int hk = h / (Hq / Hkv);
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 31, hf = lane >> 5;
-
-    const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;
-    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nk * D;
-    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
-
-    const int off = Nk - Nq;  // bottom-right causal alignment
-    const int qw = qb * T::BM + wave * T::QW;
-
-    // Q^T as the B operand: lane (n, hf) of column tile nt holds
-    // q[qw + 32 nt + n][16 kk + 8 hf .. +7]; rows past Nq read row Nq - 1 and are
-    // never stored.
-    bf16x8 qf[NT][D / 16];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const uint16_t* qrow = qbase + (size_t)min(qw + nt * 32 + n, Nq - 1) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
-    }
-
-    int kv_end = Nk;
-    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
-    const int nblk = (kv_end + T::BN - 1) / T::BN;
-    const int wave_end = CAUSAL ? min(Nk, qw + T::QW + off) : Nk;  // one past the wave's last visible key
-    const int mask_from = CAUSAL ? (qw + off) : Nk;                 // first key some wave row cannot see
-
-    f32x16 ot[NT][D / 32];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md) ot[nt][md] = zero16();
-    float m_run[NT], l_run[NT];   // running max of scale*log2(e)*s; sum over this lane's half of the keys
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        m_run[nt] = kNegInf;
-        l_run[nt] = 0.f;
-    }
-
-    // K/V staging: thread t moves 16-byte chunks t, t+256, ... of each block;
-    // 16 consecutive threads cover one key row, so every load is a full row
-    // and every LDS store is one contiguous 256-byte run.  Rows at or past
-    // kv_end are read from row kv_end - 1 (in bounds, finite, weight 0).
-    u32x4 kr[T::CPT], vr[T::CPT];
-    auto load = [&](int key0) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            const size_t g = (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8;
-            kr[r] = *reinterpret_cast<const u32x4*>(kbase + g);
-            vr[r] = *reinterpret_cast<const u32x4*>(vbase + g);
-        }
-    };
-    auto store = [&](uint16_t* sK) {
-        uint16_t* sV = sK + T::K_ELEMS;
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            *reinterpret_cast<u32x4*>(sK + row * T::KS + col8 * 8) = kr[r];
-            *reinterpret_cast<u32x4*>(sV + row * T::VS + col8 * 8) = vr[r];
-        }
-    };
-
-    load(0);
-    store(smem);
-    __syncthreads();
-
-    for (int j = 0; j < nblk; ++j) {
-        const int key0 = j * T::BN;
-        const uint16_t* sK = smem + (j & 1) * T::STAGE;
-        const uint16_t* sV = sK + T::K_ELEMS;
-        if (j + 1 < nblk) load(key0 + T::BN);
-
-        if (key0 < wave_end) {
-            // ---- S^T = K Q^T: 64 keys x QW queries -----------------------------------
-            f32x16 s[2][NT];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8 a = frag_rows(sK, T::KS, mt * 32, kk * 16, lane);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(a, qf[nt][kk], s[mt][nt]);
-                }
-            }
-            // ---- mask (only on blocks that cross the diagonal or the end) --------------
-            if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int qi = qw + nt * 32 + n;
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                            const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
-                            s[mt][nt][i] = ok ? s[mt][nt][i] : kNegInf;
-                        }
-                }
-            }
-            // ---- online softmax (base 2, lazy rescale) ----------------------------------
-            float mx[NT];
-            bool grow = false;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                float m = kNegInf;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) m = max3f(m, s[mt][nt][i], s[mt][nt][i + 1]);
-                mx[nt] = pair_max(m) * sl2;
-                grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
-            }
-            if (!wave_all(!grow)) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
-                    const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
-                    l_run[nt] *= corr;
-#pragma unroll
-                    for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) ot[nt][md][i] *= corr;
-                    m_run[nt] = m_new;
-                }
-            }
-            // P in bf16 (the matrix-core operand); l sums the same rounded values
-            // with v_dot2c_f32_bf16 against (1, 1), two per instruction.
-            bf16x8 pb[NT][T::BN / 16];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
-                float psum = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        bf16x2 pp;
-                        const float p0 = exp2_fast(__builtin_fmaf(s[mt][nt][i], sl2, -m_use));
-                        const float p1 = exp2_fast(__builtin_fmaf(s[mt][nt][i + 1], sl2, -m_use));
-                        pp[0] = (__bf16)p0;
-                        pp[1] = (__bf16)p1;
-                        if (FWD_DOT2)
-                            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
-                        else
-                            psum += p0 + p1;
-                        pb[nt][mt * 2 + (i >> 3)][i & 7] = pp[0];
-                        pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = pp[1];
-                    }
-                l_run[nt] += psum;
-            }
-            // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile) ----------
-#pragma unroll
-            for (int ks = 0; ks < T::BN / 16; ++ks)
-#pragma unroll
-                for (int md = 0; md < D / 32; ++md) {
-                    const bf16x8 a = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(a, pb[nt][ks], ot[nt][md]);
-                }
-        }
-
-        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * T::STAGE);
-        __syncthreads();
-    }
-
-    // ---- finalise: O = O / l, LSE = (m + log2 l) * ln 2 -------------------------------
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int qi = qw + nt * 32 + n;
-        const float l_tot = pair_sum(l_run[nt]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qi < Nq) {
-            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-            for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dcol = md * 32 + g * 8 + hf * 4;
-                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
-                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-                }
-            if (hf == 0)
-                LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
-        }
-    }
-}
-
-// The same pass, software pipelined inside each wave: K is staged one block
-// ahead of V, so while the exponentials of block j run on the vector ALUs the
-// scores of block j+1 are already being produced on the matrix cores (the two
-// are independent and sit in one basic block for the scheduler to interleave),
-// and O^T += V^T P^T of block j follows.  LDS holds two K and two V buffers:
-// during iteration j, K(j+1) and V(j) are read while K(j+2) and V(j+1) are
-// being loaded; one barrier per iteration.
-template <int D, int NT, bool CAUSAL>
-__device__ __forceinline__ void fwd_qblock_pipe(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                                float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b,
-                                                int h, int qb, float sl2, uint16_t* smem) {
-    using T = FwdTile<D, NT>;
-    const int hk = h / (Hq / Hkv);
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 31, hf = lane >> 5;
-
-    const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;
-    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nk * D;
-    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
-
-    const int off = Nk - Nq;
-    const int qw = qb * T::BM + wave * T::QW;
-
-    bf16x8 qf[NT][D / 16];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const uint16_t* qrow = qbase + (size_t)min(qw + nt * 32 + n, Nq - 1) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
-    }
-
-    int kv_end = Nk;
-    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
-    const int nblk = (kv_end + T::BN - 1) / T::BN;
-    const int wave_end = CAUSAL ? min(Nk, qw + T::QW + off) : Nk;
-    const int mask_from = CAUSAL ? (qw + off) : Nk;
-
-    uint16_t* sKb = smem;                       // two K buffers
-    uint16_t* sVb = smem + 2 * T::K_ELEMS;      // two V buffers
-
-    f32x16 ot[NT][D / 32];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md) ot[nt][md] = zero16();
-    float m_run[NT], l_run[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        m_run[nt] = kNegInf;
-        l_run[nt] = 0.f;
-    }
-
-    u32x4 kr[T::CPT], vr[T::CPT];
-    auto load_k = [&](int key0) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            kr[r] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8);
-        }
-    };
-    auto load_v = [&](int key0) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 8), col8 = c % (D / 8);
-            vr[r] = *reinterpret_cast<const u32x4*>(vbase + (size_t)min(key0 + row, kv_end - 1) * D + col8 * 8);
-        }
-    };
-    auto store_k = [&](uint16_t* dst) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            *reinterpret_cast<u32x4*>(dst + (c / (D / 8)) * T::KS + (c % (D / 8)) * 8) = kr[r];
-        }
-    };
-    auto store_v = [&](uint16_t* dst) {
-#pragma unroll
-        for (int r = 0; r < T::CPT; ++r) {
-            const int c = tid + 256 * r;
-            *reinterpret_cast<u32x4*>(dst + (c / (D / 8)) * T::VS + (c % (D / 8)) * 8) = vr[r];
-        }
-    };
-    auto scores = [&](const uint16_t* sK, f32x16 (&s)[2][NT]) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 a = frag_rows(sK, T::KS, mt * 32, kk * 16, lane);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(a, qf[nt][kk], s[mt][nt]);
-            }
-        }
-    };
-    // mask + row max + lazy rescale for one block of scores (VALU, may branch)
-    auto prepare = [&](f32x16 (&s)[2][NT], int key0) {
-        if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int qi = qw + nt * 32 + n;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                        const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
-                        s[mt][nt][i] = ok ? s[mt][nt][i] : kNegInf;
-                    }
-            }
-        }
-        float mx[NT];
-        bool grow = false;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            // two independent max3 chains, joined at the end
-            float m0 = kNegInf, m1 = kNegInf;
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                m0 = max3f(m0, s[0][nt][i], s[0][nt][i + 1]);
-                m1 = max3f(m1, s[1][nt][i], s[1][nt][i + 1]);
-            }
-            mx[nt] = pair_max(__builtin_fmaxf(m0, m1)) * sl2;
-            grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
-        }
-        if (!wave_all(!grow)) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
-                const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
-                l_run[nt] *= corr;
-#pragma unroll
-                for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ot[nt][md][i] *= corr;
-                m_run[nt] = m_new;
-            }
-        }
-    };
-    // exponentials -> bf16 P and the row-sum update (VALU only, no branch)
-    auto exponentiate = [&](const f32x16 (&s)[2][NT], bf16x8 (&pb)[NT][T::BN / 16]) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
-            float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = exp2_fast(__builtin_fmaf(s[mt][nt][i], sl2, -m_use));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[mt][nt][i + 1], sl2, -m_use));
-                    ps0 += p0;
-                    ps1 += p1;
-                    pb[nt][mt * 2 + (i >> 3)][i & 7] = (__bf16)p0;
-                    pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)p1;
-                }
-            l_run[nt] += ps0 + ps1;
-        }
-    };
-    auto accumulate = [&](const uint16_t* sV, const bf16x8 (&pb)[NT][T::BN / 16]) {
-#pragma unroll
-        for (int ks = 0; ks < T::BN / 16; ++ks)
-#pragma unroll
-            for (int md = 0; md < D / 32; ++md) {
-                const bf16x8 a = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(a, pb[nt][ks], ot[nt][md]);
-            }
-    };
-
-    // ---- prologue: K(0), V(0), K(1) into LDS; S(0) ----------------------------------
-    load_k(0);
-    load_v(0);
-    store_k(sKb);
-    store_v(sVb);
-    if (nblk > 1) {
-        load_k(T::BN);
-        store_k(sKb + T::K_ELEMS);
-    }
-    __syncthreads();
-    f32x16 s_cur[2][NT], s_nxt[2][NT];
-    if (0 < wave_end) scores(sKb, s_cur);
-
-    for (int j = 0; j < nblk; ++j) {
-        const int key0 = j * T::BN;
-        const bool have_v = j + 1 < nblk, have_k = j + 2 < nblk;
-        if (have_v) load_v(key0 + T::BN);
-        if (have_k) load_k(key0 + 2 * T::BN);
-        const bool do_cur = key0 < wave_end;
-        const bool do_nxt = have_v && key0 + T::BN < wave_end;
-        const uint16_t* sKn = sKb + ((j + 1) & 1) * T::K_ELEMS;
-        const uint16_t* sV = sVb + (j & 1) * T::V_ELEMS;
-        if (do_cur) {
-            prepare(s_cur, key0);
-            bf16x8 pb[NT][T::BN / 16];
-            if (do_nxt && FWD_SCHED && D == 64) {
-                // One basic block, scheduled explicitly: every LDS fragment of
-                // K(j+1) and V(j) is requested first, then each score MFMA of
-                // block j+1 is followed by a group of vector instructions of the
-                // exponentials of block j (the matrix core runs the MFMA while
-                // the wave keeps issuing), then O^T += V^T P^T of block j.
-                constexpr int NKF = 2 * (D / 16), NVF = (T::BN / 16) * (D / 32);
-                bf16x8 kfr[2][D / 16], vfr[T::BN / 16][D / 32];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < D / 16; ++kk) kfr[mt][kk] = frag_rows(sKn, T::KS, mt * 32, kk * 16, lane);
-#pragma unroll
-                for (int ks = 0; ks < T::BN / 16; ++ks)
-#pragma unroll
-                    for (int md = 0; md < D / 32; ++md) vfr[ks][md] = frag_tr(sV, T::VS, ks * 16, md * 32, lane);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s_nxt[mt][nt] = zero16();
-#pragma unroll
-                    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            s_nxt[mt][nt] = mfma32x32x16(kfr[mt][kk], qf[nt][kk], s_nxt[mt][nt]);
-                }
-                exponentiate(s_cur, pb);
-#pragma unroll
-                for (int ks = 0; ks < T::BN / 16; ++ks)
-#pragma unroll
-                    for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            ot[nt][md] = mfma32x32x16(vfr[ks][md], pb[nt][ks], ot[nt][md]);
-                // schedule: LDS reads, a few VALU, then (MFMA, VALU group) pairs
-                constexpr int NQK = 2 * (D / 16) * NT;
-                constexpr int VPER = (120 * NT + NQK - 1) / NQK;
-                __builtin_amdgcn_sched_group_barrier(0x100, NKF + 2 * NVF, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
-                static_for<0, NQK>([&](auto) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x402, VPER, 0);
-                });
-                __builtin_amdgcn_sched_group_barrier(0x008, (T::BN / 16) * (D / 32) * NT, 0);
-            } else {
-                if (do_nxt) scores(sKn, s_nxt);
-                exponentiate(s_cur, pb);
-                accumulate(sV, pb);
-            }
-        }
-        if (have_v) store_v(sVb + ((j + 1) & 1) * T::V_ELEMS);
-        if (have_k) store_k(sKb + (j & 1) * T::K_ELEMS);
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) s_cur[mt][nt] = s_nxt[mt][nt];
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int qi = qw + nt * 32 + n;
-        const float l_tot = pair_sum(l_run[nt]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qi < Nq) {
-            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-            for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dcol = md * 32 + g * 8 + hf * 4;
-                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
-                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-                }
-            if (hf == 0)
-                LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Ring variant: K/V blocks travel global -> LDS with direct-to-LDS loads
@@ -1184,33 +654,6 @@ __global__ __launch_bounds__(NW * 64, SP_WPE) void fwd_sp_kernel(
     }
 }
 
-// Grid: (query-block slot, batch*head) flattened with batch*head fastest, so
-// the blocks of one (batch, head) are BH launch slots apart (the same XCD
-// when BH is a multiple of 8) and share its L2 copy of K and V.  Causal: slot
-// p processes query blocks p and nqb-1-p, so every workgroup does the same
-// amount of work (nqb+1 half-blocks of keys) and no long tail is left.
-template <int D, int NT, bool CAUSAL>
-__global__ __launch_bounds__(256, (D * NT > 128 ? 1 : 2)) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
-    float sl2) {
-    extern __shared__ __align__(16) uint16_t smem[];
-    const int slot = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
-    const int b = bh / Hq, h = bh % Hq;
-    if (!CAUSAL || !FWD_PAIR) {
-        FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, CAUSAL ? nqb - 1 - slot : slot, sl2,
-                                  smem);
-        return;
-    }
-    const int heavy = nqb - 1 - slot;
-    FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, heavy, sl2, smem);
-    if (slot != heavy) {
-        __syncthreads();
-        FWD_QBLOCK<D, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, slot, sl2, smem);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // float32 forward: the same recurrence on the vector ALUs, four lanes per query
 // row (each owns d/4 columns).  Also serves float32 decode through kv_lens.
@@ -1300,22 +743,6 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, int NT, bool CAUSAL>
-static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-    using T = FwdTile<D, NT>;
-    const int nqb = (a.Nq + T::BM - 1) / T::BM;
-    const int slots = (CAUSAL && FWD_PAIR) ? (nqb + 1) / 2 : nqb;
-    const int BH = a.B * a.Hq;
-    auto kern = fwd_bf16_kernel<D, NT, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots * BH), dim3(256), T::LDS_BYTES, (hipStream_t)a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, a.scale * kLog2e);
-    return hipGetLastError();
-}
-
 template <int D, int NW, int S, int NT, bool CAUSAL>
 static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
     using T = RingTile<D, NW, S, NT>;
@@ -1351,16 +778,13 @@ hipError_t launch_fwd_bf16(const FwdArgs& a) {
 #if FWD_SP
     if (a.d == 64) return a.causal ? launch_fwd_sp_t<64, SP_NW64, true>(a) : launch_fwd_sp_t<64, SP_NW64, false>(a);
     return a.causal ? launch_fwd_sp_t<128, SP_NW128, true>(a) : launch_fwd_sp_t<128, SP_NW128, false>(a);
-#endif
-#if FWD_RING
+#else
     if (a.d == 64)
         return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, true>(a)
                         : launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, false>(a);
     return a.causal ? launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, true>(a)
                     : launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, false>(a);
 #endif
-    if (a.d == 64) return a.causal ? launch_fwd_bf16_t<64, FWD_NT64, true>(a) : launch_fwd_bf16_t<64, FWD_NT64, false>(a);
-    return a.causal ? launch_fwd_bf16_t<128, FWD_NT128, true>(a) : launch_fwd_bf16_t<128, FWD_NT128, false>(a);
 }
 
 template <int D>
