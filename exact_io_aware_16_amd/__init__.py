@@ -8,7 +8,9 @@ no fallback of any kind.  PyTorch only provides device memory and streams.
 
 Low-level entry points mirror the C names (``fa_fwd``, ``fa_bwd``,
 ``fa_decode``, ``fa_bwd_workspace_bytes``, ``fa_decode_workspace_bytes``) and
-write into caller-provided tensors.  ``fwd``, ``bwd`` and ``decode`` allocate
+write into caller-provided tensors; ``prepare_fwd`` / ``prepare_bwd`` /
+``prepare_decode`` do the checks and marshalling once and return a callable
+that only launches (for tight loops).  ``fwd``, ``bwd`` and ``decode`` allocate
 their outputs with torch and call them.
 """
 from __future__ import annotations
@@ -113,18 +115,27 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d) -> int:
     return load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)
 
 
-def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
-    """O = softmax(scale Q K^T [+causal]) V into ``o``; row logsumexp into ``lse``."""
+def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
+    """Check and marshal the arguments of fa_fwd once; returns a zero-argument
+    callable that launches it (the tensors must stay alive and unchanged in
+    shape).  Raises on a non-zero status when called."""
     _dev(q, k, v, o, lse)
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
-                                 _dtype_code(q), scale, int(bool(causal)), _stream(stream)))
+    lib = load_library()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q), scale,
+            int(bool(causal)), _stream(stream))
+    return lambda: _check(lib.fa_fwd(*args))
 
 
-def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
-    """Gradients of sum(O * dO) into dq, dk, dv (their dtype picks the gradient dtype)."""
+def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
+    """O = softmax(scale Q K^T [+causal]) V into ``o``; row logsumexp into ``lse``."""
+    prepare_fwd(q, k, v, o, lse, causal=causal, scale=scale, stream=stream)()
+
+
+def prepare_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
+    """fa_bwd's arguments checked and marshalled once (see prepare_fwd)."""
     _dev(q, k, v, o, dO, lse, dq, dk, dv, workspace)
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -132,14 +143,20 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None,
     gcode = _dtype_code(dq)
     if _dtype_code(dk) != gcode or _dtype_code(dv) != gcode:
         raise TypeError("dq, dk, dv must share one dtype")
-    _check(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), gcode, B, Hq, Hkv, Nq, Nk, d, _dtype_code(q), scale,
-                                 int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream)))
+    lib = load_library()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), gcode, B, Hq,
+            Hkv, Nq, Nk, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return lambda: _check(lib.fa_bwd(*args))
 
 
-def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
-    """One query token per head against the first seqlens[b] cached keys."""
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
+    """Gradients of sum(O * dO) into dq, dk, dv (their dtype picks the gradient dtype)."""
+    prepare_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=causal, scale=scale, stream=stream)()
+
+
+def prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
+    """fa_decode's arguments checked and marshalled once (see prepare_fwd)."""
     _dev(q, k_cache, v_cache, seqlens, o, lse, workspace)
     torch = _torch()
     if seqlens.dtype != torch.int32:
@@ -147,9 +164,15 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, strea
     B, Hq, _, d = q.shape
     _, Hkv, Nmax, _ = k_cache.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(load_library().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
-                                    B, Hq, Hkv, Nmax, d, _dtype_code(q), scale, _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    lib = load_library()
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nmax, d,
+            _dtype_code(q), scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return lambda: _check(lib.fa_decode(*args))
+
+
+def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
+    """One query token per head against the first seqlens[b] cached keys."""
+    prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=scale, stream=stream)()
 
 
 # ---------------------------------------------------------------------------
