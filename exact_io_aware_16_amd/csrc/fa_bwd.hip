@@ -155,9 +155,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 #pragma unroll
     for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
-    for (int j = 0; j < nblk; ++j) {
+    // Block j uses ring slot j % NS; unrolled NS times so the slot is a
+    // compile-time constant (LDS addresses: per-lane base plus immediates).
+    auto block = [&](int j, auto slc) {
+        constexpr int slot = decltype(slc)::value;
         const int key0 = j * T::BN;
-        const int slot = j % T::NS;
         // this wave's loads of block j are done once at most NS-2 younger stages remain
         wait_vmcnt<(T::NS - 2) * T::LPS>();
         __builtin_amdgcn_s_barrier();
@@ -204,6 +206,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                     acc[md] = mfma32x32x16(frag_tr_swz<D>(sK, ks * 16, md * 32, lane), db, acc[md]);
             }
         }
+    };
+    for (int j0 = 0; j0 < nblk; j0 += T::NS) {
+        static_for<0, T::NS>([&](auto slc) {
+            if (j0 + decltype(slc)::value < nblk) block(j0 + decltype(slc)::value, slc);
+        });
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
@@ -319,8 +326,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
     }
-    for (int stp = 0; stp < total; ++stp) {
-        const int slot = stp % T::NS;
+    // Step stp uses ring slot stp % NS; the loop is unrolled NS times so the
+    // slot is a compile-time constant (LDS addresses: per-lane base plus
+    // immediate offsets).
+    auto step = [&](int stp, auto slc) {
+        constexpr int slot = decltype(slc)::value;
         // this wave's loads of step stp are done once at most NS-2 younger stages remain
         wait_vmcnt<(T::NS - 2) * T::LPS>();
         __builtin_amdgcn_s_barrier();
@@ -388,6 +398,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                 }
             }
         }
+    };
+    for (int s0 = 0; s0 < total; s0 += T::NS) {
+        static_for<0, T::NS>([&](auto slc) {
+            if (s0 + decltype(slc)::value < total) step(s0 + decltype(slc)::value, slc);
+        });
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
