@@ -44,7 +44,7 @@
 #define RING_NW128 8     // waves per workgroup, d = 128
 #endif
 #ifndef RING_S128
-#define RING_S128 4      // ring stages, d = 128
+#define RING_S128 2      // ring stages, d = 128
 #endif
 #ifndef RING_NT64
 #define RING_NT64 1      // 32-query column tiles per wave, d = 64
@@ -191,12 +191,12 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) issue(st, st);
 
-    // Block j uses ring stage j % S.  For d = 64 the loop is unrolled S times so
-    // that the stage is a compile-time constant: LDS fragment addresses become
-    // one per-lane base plus immediate offsets (d = 128 has no registers to
-    // spare for the larger unrolled body).
+    // Block j uses ring stage j % S.  The loop is unrolled S times so that the
+    // stage is a compile-time constant: LDS fragment addresses become one
+    // per-lane base plus immediate offsets (with a run-time stage the compiler
+    // keeps a set of addresses per stage live).
     auto block = [&](int j, auto stc) {
-        const int st = decltype(stc)::value < 0 ? j % S : decltype(stc)::value;
+        constexpr int st = decltype(stc)::value;
         // this wave's loads of block j are done once at most (S-2) stages remain outstanding
         wait_vmcnt<(S - 2) * T::LPS>();
         __builtin_amdgcn_s_barrier();
@@ -316,14 +316,10 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
             }
         }
     };
-    if constexpr (D == 64) {
-        for (int j0 = 0; j0 < nblk; j0 += S) {
-            static_for<0, S>([&](auto stc) {
-                if (j0 + decltype(stc)::value < nblk) block(j0 + decltype(stc)::value, stc);
-            });
-        }
-    } else {
-        for (int j = 0; j < nblk; ++j) block(j, std::integral_constant<int, -1>{});
+    for (int j0 = 0; j0 < nblk; j0 += S) {
+        static_for<0, S>([&](auto stc) {
+            if (j0 + decltype(stc)::value < nblk) block(j0 + decltype(stc)::value, stc);
+        });
     }
     // drain the ring's trailing loads before the workgroup's LDS is reused
     wait_vmcnt<0>();
