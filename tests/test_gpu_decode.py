@@ -99,3 +99,37 @@ def test_decode_equals_forward_with_one_query():
     o_f, l_f = fa.fwd(q, k, v, causal=False, scale=w.scale)
     assert np.abs(o_dec - to_host(o_f)).max() <= 2e-2
     assert np.abs(l_dec - to_host(l_f)[:, :, 0]).max() <= 2e-2
+
+
+def test_decode_workspace_needs_no_initialisation_and_is_reusable():
+    """The caller's workspace needs no initialisation and may be reused: random
+    bytes or all-ones before a call, then the same buffer for calls with other
+    lengths and for a smaller shape, whose partial results and stage prefixes
+    then sit where the previous call left other data."""
+    import torch
+    B, Hq, Hkv, Nmax, d = 5, 8, 2, 3000, 128
+    w = W.random_case(21, B, Hq, Hkv, 1, Nmax, d)
+    qd, kd, vd = (to_device(w.tensors[n]) for n in ("q", "k", "v"))
+    ws = fa.decode_workspace(qd, kd)
+    rng = np.random.default_rng(5)
+    q, k, v = w.values("q"), w.values("k"), w.values("v")
+
+    def check(lens, fill=None, qx=qd, kx=kd, vx=vd, ref=(q, k, v)):
+        if fill is not None:
+            ws.copy_(torch.from_numpy(fill).to(ws.device))
+        announce(f"decode workspace reuse: lens {list(lens)}, fill {'kept' if fill is None else 'new'}")
+        ld = to_device(np.asarray(lens, dtype=np.int32))
+        o, lse = fa.decode(qx, kx, vx, ld, scale=w.scale, workspace=ws)
+        O, L = oracle.ref_decode(*ref, np.asarray(lens), scale=w.scale)
+        assert_close("O", to_host(o), O, TOL_BF16)
+        assert_close("LSE", to_host(lse), L, TOL_BF16)
+
+    n = ws.numel()
+    check([3000, 1, 2999, 64, 1500], fill=rng.integers(0, 256, n, dtype=np.uint8))
+    check([100, 3000, 0, 33, 2048])
+    check([3000, 3000, 3000, 3000, 3000], fill=np.full(n, 0xFF, dtype=np.uint8))
+    check([7, 8, 9, 10, 11])
+    # a smaller batch and group in the same workspace
+    q2, k2, v2 = q[:2, :4], k[:2, :1], v[:2, :1]
+    check([2500, 900], qx=qd[:2, :4].contiguous(), kx=kd[:2, :1].contiguous(), vx=vd[:2, :1].contiguous(),
+          ref=(q2, k2, v2))
