@@ -31,8 +31,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
-// (1.0, 1.0) in bf16, the second operand of row sums done with v_dot2c_f32_bf16.
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -64,28 +64,6 @@
 #ifndef RING_WPE64
 #define RING_WPE64 2
 #endif
-// Software-pipelined kernel (fwd_sp_kernel) instead of the ring kernel: its
-// waves per workgroup and minimum waves per SIMD; SP_PIN keeps each chunk of
-// exponentials next to its MFMA; SP_PAIR pairs causal query blocks.
-#ifndef FWD_SP
-#define FWD_SP 0
-#endif
-#ifndef SP_NW64
-#define SP_NW64 4
-#endif
-#ifndef SP_NW128
-#define SP_NW128 8
-#endif
-#ifndef SP_WPE
-#define SP_WPE 2
-#endif
-#ifndef SP_PIN
-#define SP_PIN 1
-#endif
-#ifndef SP_PAIR
-#define SP_PAIR 1
-#endif
-
 namespace fa {
 
 // Lazy rescaling threshold (log2 units): the running max is only raised when
@@ -120,7 +98,7 @@ struct RingTile {
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // sched_group_barrier masks
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 template <int D, int NW, int S, int NT, bool CAUSAL>
 __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -361,296 +339,6 @@ __global__ __launch_bounds__(NW * 64, ((NW == 4 && D * NT <= 128) ? RING_WPE64 :
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined variant.  Per wave and block j the work has a matrix
-// part (S = K Q^T, O^T += V^T P^T) and a vector part (row max, exponentials,
-// bf16 packing, row sums).  Inside one block they depend on each other, so
-// the loop is skewed by one block: while the matrix cores compute S(j+1), the
-// vector units exponentiate S(j); then O^T += V^T P(j)^T runs while the row
-// maximum of S(j+1) is formed.  The two halves are interleaved instruction
-// by instruction with sched_group_barrier.  K and V travel in separate
-// three-slot rings (K one block further ahead, since S(j+1) needs K(j+1)
-// while P(j) still needs V(j)), filled by direct-to-LDS loads two blocks
-// ahead with one barrier per block.  Row sums take the bf16-rounded P with
-// v_dot2_f32_bf16 against (1, 1), so numerator and denominator use the same
-// probabilities.
-// ---------------------------------------------------------------------------
-template <int D, int NW>
-struct SpTile {
-    static constexpr int QW = 32;                  // query rows per wave
-    static constexpr int BM = QW * NW;             // query rows per workgroup
-    static constexpr int BN = 64;                  // keys per block
-    static constexpr int TILE = BN * D;            // elements of one K (or V) block
-    static constexpr int NSLOT = 3;
-    static constexpr int LDS_BYTES = 2 * NSLOT * TILE * 2;
-    static constexpr int IPW = (BN * D / 8) / 64 / NW;   // load instructions per wave per tile
-    static_assert(IPW >= 1 && (BN * D / 8) % (64 * NW) == 0, "tile must split evenly over the waves");
-    static_assert(4 * IPW < 64, "vmcnt range");
-};
-
-
-template <int D, int NW, bool CAUSAL>
-__device__ __forceinline__ void fwd_qblock_sp(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                              float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int b,
-                                              int h, int qb, float sl2, uint16_t* smem) {
-    using T = SpTile<D, NW>;
-    const int hk = h / (Hq / Hkv);
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int n = lane & 31, hf = lane >> 5;
-    uint16_t* sKr = smem;                         // [NSLOT][TILE]
-    uint16_t* sVr = smem + T::NSLOT * T::TILE;    // [NSLOT][TILE]
-
-    const uint16_t* qbase = Q + (size_t)(b * Hq + h) * Nq * D;
-    const uint16_t* kbase = K + (size_t)(b * Hkv + hk) * Nk * D;
-    const uint16_t* vbase = V + (size_t)(b * Hkv + hk) * Nk * D;
-
-    const int off = Nk - Nq;
-    const int qw = qb * T::BM + wave * T::QW;
-    const int qi = qw + n;
-
-    // Q^T as the B operand: lane (n, hf) holds query qw + n (rows past Nq read
-    // row Nq - 1 and are never stored)
-    bf16x8 qf[D / 16];
-    {
-        const uint16_t* qrow = qbase + (size_t)min(qi, Nq - 1) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hf * 8));
-    }
-
-    int kv_end = Nk;
-    if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
-    const int nblk = (kv_end + T::BN - 1) / T::BN;
-    // blocks this wave computes (its last query row sees keys < qw + 32 + off)
-    const int wave_end = CAUSAL ? min(kv_end, qw + T::QW + off) : kv_end;
-    const int nblk_w = wave_end > 0 ? (wave_end + T::BN - 1) / T::BN : 0;
-    const int mask_from = CAUSAL ? (qw + off) : Nk;
-
-    // This wave's share of a K or V block (rows clamped to kv_end - 1, so
-    // blocks past the end reload a valid row and keep the load count fixed).
-    auto issue_tile = [&](const uint16_t* base, uint16_t* tile, int blk) {
-#pragma unroll
-        for (int i = 0; i < T::IPW; ++i) {
-            const int slot = (wave * T::IPW + i) * 64 + lane;
-            const int row = slot / (D / 8), pos = slot % (D / 8);
-            const size_t g = (size_t)min(blk * T::BN + row, kv_end - 1) * D + ((pos ^ swz<D>(row)) << 3);
-            __builtin_amdgcn_global_load_lds(base + g, LDS_PTR(tile + (wave * T::IPW + i) * 64 * 8), 16, 0, 0);
-        }
-    };
-    auto issueK = [&](int blk) { issue_tile(kbase, sKr + (blk % T::NSLOT) * T::TILE, blk); };
-    auto issueV = [&](int blk) { issue_tile(vbase, sVr + (blk % T::NSLOT) * T::TILE, blk); };
-
-    constexpr int NK = 2 * (D / 16);   // S MFMAs per block (2 key halves x D/16 k-steps)
-    constexpr int NV = 4 * (D / 32);   // PV MFMAs per block (4 key groups x D/32 column tiles)
-    constexpr int AH = 4;              // LDS fragment reads issued ahead of their MFMA
-    auto kfrag = [&](const uint16_t* sK, int i) {   // i = mt * (D/16) + kk
-        return frag_rows_swz<D>(sK, (i / (D / 16)) * 32, (i % (D / 16)) * 16, lane);
-    };
-    auto vfrag = [&](const uint16_t* sV, int i) {   // i = ks * (D/32) + md
-        return frag_tr_swz<D>(sV, (i / (D / 32)) * 16, (i % (D / 32)) * 32, lane);
-    };
-    auto mask = [&](int blk, f32x16 (&sc)[2]) {
-        const int key0 = blk * T::BN;
-        if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + mt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                    const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
-                    sc[mt][i] = ok ? sc[mt][i] : kNegInf;
-                }
-        }
-    };
-    float m_run = kNegInf, l_run = 0.f;
-    f32x16 ot[D / 32];
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md) ot[md] = zero16();
-
-    // exponentials of elements [e0, e0 + ne) of S (flat index mt * 16 + i),
-    // packed into P and summed with dot2 against (1, 1)
-    auto exp_part = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], float& psum, float m_use, int e0, int ne) {
-#pragma unroll
-        for (int e = e0; e < e0 + ne; e += 2) {
-            const int mt = e >> 4, i = e & 15;
-            bf16x2 pp;
-            pp[0] = (__bf16)exp2_fast(__builtin_fmaf(sc[mt][i], sl2, -m_use));
-            pp[1] = (__bf16)exp2_fast(__builtin_fmaf(sc[mt][i + 1], sl2, -m_use));
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
-            pb[mt * 2 + (i >> 3)][i & 7] = pp[0];
-            pb[mt * 2 + (i >> 3)][(i & 7) + 1] = pp[1];
-            // keep the chunk here: without a use at this point the compiler
-            // sinks the exponentials to the matrix products that consume P
-            if (SP_PIN) asm volatile("" ::"v"(__builtin_bit_cast(uint32_t, pp)));
-        }
-    };
-    // running max over elements [e0, e0 + ne) of S
-    auto max_part = [&](const f32x16 (&sc)[2], float& m0, int e0, int ne) {
-#pragma unroll
-        for (int e = e0; e < e0 + ne; e += 2) m0 = max3f(m0, sc[e >> 4][e & 15], sc[e >> 4][(e & 15) + 1]);
-    };
-    // fold a new block maximum in: rescale l and O (lazy: only past the threshold)
-    auto rescale = [&](float mx) {
-        if (!wave_all(mx <= m_run + kRescaleThreshold)) {
-            const float m_new = __builtin_fmaxf(m_run, mx);
-            const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
-            l_run *= corr;
-#pragma unroll
-            for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) ot[md][i] *= corr;
-            m_run = m_new;
-        }
-    };
-    auto m_use_now = [&]() { return (m_run == kNegInf) ? 0.f : m_run; };
-
-    // S(blk) alone (prologue, and waves whose previous block was their last)
-    auto qk_only = [&](int blk, f32x16 (&sn)[2]) {
-        const uint16_t* sK = sKr + (blk % T::NSLOT) * T::TILE;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) sn[mt] = zero16();
-#pragma unroll
-        for (int i = 0; i < NK; ++i) sn[i / (D / 16)] = mfma32x32x16(kfrag(sK, i), qf[i % (D / 16)], sn[i / (D / 16)]);
-        mask(blk, sn);
-        float m0 = kNegInf;
-        max_part(sn, m0, 0, 32);
-        rescale(pair_max(m0) * sl2);
-    };
-    // P(j) and O += V^T P(j)^T alone (a wave's last block)
-    auto pv_only = [&](int j, const f32x16 (&sc)[2]) {
-        const uint16_t* sV = sVr + (j % T::NSLOT) * T::TILE;
-        bf16x8 pb[4];
-        float psum = 0.f;
-        exp_part(sc, pb, psum, m_use_now(), 0, 32);
-        l_run += psum;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) ot[i % (D / 32)] = mfma32x32x16(vfrag(sV, i), pb[i / (D / 32)], ot[i % (D / 32)]);
-    };
-    // The steady state, written in issue order: S(j+1) MFMAs alternate with
-    // chunks of P(j)'s exponentials, then O += V^T P(j)^T MFMAs alternate with
-    // chunks of S(j+1)'s row maximum; fragment reads run AH MFMAs ahead.
-    // sched_barrier keeps the compiler from regrouping the chunks.
-    auto full = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const uint16_t* sK = sKr + ((j + 1) % T::NSLOT) * T::TILE;
-        const uint16_t* sV = sVr + (j % T::NSLOT) * T::TILE;
-        bf16x8 pb[4];
-        float psum = 0.f;
-        const float m_use = m_use_now();
-        bf16x8 kf[NK];
-#pragma unroll
-        for (int i = 0; i < AH; ++i) kf[i] = kfrag(sK, i);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) sn[mt] = zero16();
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if (i + AH < NK) kf[i + AH] = kfrag(sK, i + AH);
-            sn[i / (D / 16)] = mfma32x32x16(kf[i], qf[i % (D / 16)], sn[i / (D / 16)]);
-            exp_part(sc, pb, psum, m_use, i * (32 / NK), 32 / NK);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        l_run += psum;
-        mask(j + 1, sn);
-        bf16x8 vf[NV];
-#pragma unroll
-        for (int i = 0; i < AH; ++i) vf[i] = vfrag(sV, i);
-        float m0 = kNegInf;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if (i + AH < NV) vf[i + AH] = vfrag(sV, i + AH);
-            ot[i % (D / 32)] = mfma32x32x16(vf[i], pb[i / (D / 32)], ot[i % (D / 32)]);
-            max_part(sn, m0, i * (32 / NV), 32 / NV);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        rescale(pair_max(m0) * sl2);
-    };
-    auto sync_issue = [&](int j) {
-        // K(j+1), V(j) were issued two blocks ago; V(j+1), K(j+2) may still fly
-        wait_vmcnt<2 * T::IPW>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issueV(j + 2);
-        issueK(j + 3);
-    };
-
-    // prologue: K0 V0 K1 V1 K2 in flight; S(0) once K0 has landed
-    issueK(0);
-    issueV(0);
-    issueK(1);
-    issueV(1);
-    issueK(2);
-    f32x16 sA[2], sB[2];
-    wait_vmcnt<4 * T::IPW>();
-    __builtin_amdgcn_s_barrier();
-    if (nblk_w > 0) qk_only(0, sA);
-
-    // invariant at the top of the first loop: sA = S(j)
-    int j = 0;
-    for (; j + 2 < nblk_w; j += 2) {
-        sync_issue(j);
-        full(j, sA, sB);
-        sync_issue(j + 1);
-        full(j + 1, sB, sA);
-    }
-    if (j + 1 < nblk_w) {
-        sync_issue(j);
-        full(j, sA, sB);
-        sync_issue(j + 1);
-        pv_only(j + 1, sB);
-        j += 2;
-    } else if (j < nblk_w) {
-        sync_issue(j);
-        pv_only(j, sA);
-        j += 1;
-    }
-    // blocks past this wave's last key: keep the workgroup's loads and barriers
-    for (; j < nblk; ++j) sync_issue(j);
-    // drain the trailing loads before the workgroup's LDS is reused
-    wait_vmcnt<0>();
-
-    const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qi < Nq) {
-        uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dcol = md * 32 + g * 8 + hf * 4;
-                const uint32_t lo = pack_bf16x2(ot[md][g * 4 + 0] * inv, ot[md][g * 4 + 1] * inv);
-                const uint32_t hi = pack_bf16x2(ot[md][g * 4 + 2] * inv, ot[md][g * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-            }
-        if (hf == 0)
-            LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
-    }
-}
-
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, SP_WPE) void fwd_sp_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
-    float sl2) {
-    extern __shared__ __align__(16) uint16_t smem[];
-    const int slot = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
-    if (!CAUSAL || !SP_PAIR) {
-        fwd_qblock_sp<D, NW, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, bh / Hq, bh % Hq,
-                                     CAUSAL ? nqb - 1 - slot : slot, sl2, smem);
-        return;
-    }
-    // causal: slot p takes query blocks nqb-1-p and p, so every workgroup has
-    // the same number of key blocks and a single wave of workgroups covers the
-    // grid without a tail of light blocks
-    const int heavy = nqb - 1 - slot;
-    fwd_qblock_sp<D, NW, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, bh / Hq, bh % Hq, heavy, sl2, smem);
-    if (slot < heavy) {
-        __builtin_amdgcn_s_barrier();   // every wave is done with the ring before it is refilled
-        fwd_qblock_sp<D, NW, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, bh / Hq, bh % Hq, slot, sl2, smem);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // float32 forward: the same recurrence on the vector ALUs, four lanes per query
 // row (each owns d/4 columns).  Also serves float32 decode through kv_lens.
 // ---------------------------------------------------------------------------
@@ -754,33 +442,12 @@ static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-template <int D, int NW, bool CAUSAL>
-static hipError_t launch_fwd_sp_t(const FwdArgs& a) {
-    using T = SpTile<D, NW>;
-    const int nqb = (a.Nq + T::BM - 1) / T::BM;
-    const int BH = a.B * a.Hq;
-    const int slots = (CAUSAL && SP_PAIR) ? (nqb + 1) / 2 : nqb;
-    auto kern = fwd_sp_kernel<D, NW, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots * BH), dim3(NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, a.scale * kLog2e);
-    return hipGetLastError();
-}
-
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-#if FWD_SP
-    if (a.d == 64) return a.causal ? launch_fwd_sp_t<64, SP_NW64, true>(a) : launch_fwd_sp_t<64, SP_NW64, false>(a);
-    return a.causal ? launch_fwd_sp_t<128, SP_NW128, true>(a) : launch_fwd_sp_t<128, SP_NW128, false>(a);
-#else
     if (a.d == 64)
         return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, true>(a)
                         : launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, false>(a);
     return a.causal ? launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, true>(a)
                     : launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, false>(a);
-#endif
 }
 
 template <int D>
