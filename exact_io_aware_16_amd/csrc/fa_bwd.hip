@@ -251,13 +251,17 @@ template <int D, bool CAUSAL, typename G>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
-    G* __restrict__ dK, G* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkb, float sl2, float scale) {
+    G* __restrict__ dK, G* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int BHK, float sl2, float scale) {
     using T = DkvTile<D>;
     extern __shared__ __align__(16) uint16_t smem[];
     const int id = blockIdx.x;
-    // key blocks near the start see the most queries under the causal mask: issue them first
-    const int kblk = id % nkb;
-    const int bhk = id / nkb;
+    // Key blocks near the start see the most queries under the causal mask,
+    // so launch slot id takes key block id / BHK: every (batch, K/V head)'s
+    // heaviest block goes first.  The blocks of one (batch, head) are BHK
+    // slots apart, so with BHK a multiple of 8 they share an XCD and its L2
+    // copy of Q and dO.
+    const int kblk = id / BHK;
+    const int bhk = id % BHK;
     const int b = bhk / Hkv, hk = bhk % Hkv;
     const int g = Hq / Hkv;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -616,7 +620,7 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(nkb * a.B * a.Hkv), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, lse2, a.delta,
-                           (G*)a.dk, (G*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, nkb, sl2, a.scale);
+                           (G*)a.dk, (G*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, a.B * a.Hkv, sl2, a.scale);
     }
     return hipGetLastError();
 }
