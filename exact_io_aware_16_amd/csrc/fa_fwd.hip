@@ -442,10 +442,26 @@ static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
     return hipGetLastError();
 }
 
+// d = 64 with two 32-query column tiles per wave: every K and V fragment read
+// from LDS feeds two MFMAs, which pays once there are enough workgroups
+// (workgroups of 256 queries, 2 per CU) to fill the chip past the causal tail;
+// smaller grids keep one tile per wave (more, lighter workgroups).
+static bool fwd64_two_tiles(const FwdArgs& a) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    using T2 = RingTile<64, RING_NW64, RING_S64, 2>;
+    const long long wgs = (long long)((a.Nq + T2::BM - 1) / T2::BM) * a.B * a.Hq;
+    return wgs >= (long long)(a.causal ? 4 : 2) * ncu;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    if (a.d == 64)
+    if (a.d == 64) {
+        if (fwd64_two_tiles(a))
+            return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, 2, true>(a)
+                            : launch_fwd_ring_t<64, RING_NW64, RING_S64, 2, false>(a);
         return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, true>(a)
                         : launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, false>(a);
+    }
     return a.causal ? launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, true>(a)
                     : launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, false>(a);
 }

@@ -60,6 +60,24 @@ def test_config5_forward_sampled_rows():
     assert_close("LSE[rows]", np.array([lse[b, h, i] for b, h, i in rows]), L, TOL_BF16)
 
 
+@pytest.mark.parametrize("shape", [
+    # (B, Hq, Hkv, Nq, Nk, d, causal): grids large enough for two query tiles per wave at d = 64
+    (1, 32, 32, 4096, 4096, 64, False),
+    (1, 64, 8, 4000, 4000, 64, True),     # GQA g=8, ragged last query block
+], ids=lambda s: "B{}H{}x{}N{}x{}d{}{}".format(*s[:6], "c" if s[6] else ""))
+def test_d64_large_grids_sampled_rows(shape):
+    """The d = 64 kernel takes two 32-query tiles per wave on large grids; 512
+    sampled rows against the oracle (the small shapes elsewhere take one)."""
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    w = W.random_case(sum(shape[:6]), B, Hq, Hkv, Nq, Nk, d)
+    announce(f"d64 large grid {shape}")
+    o, lse = run_fwd(w, causal)
+    rows = W.sampled_query_rows(7, B, Hq, Nq, 512)
+    O, L = oracle.ref_fwd_rows(w.values("q"), w.values("k"), w.values("v"), rows, causal=causal, scale=w.scale)
+    assert_close("O[rows]", np.stack([o[b, h, i] for b, h, i in rows]), O, TOL_BF16)
+    assert_close("LSE[rows]", np.array([lse[b, h, i] for b, h, i in rows]), L, TOL_BF16)
+
+
 SHAPES = [
     # (B, Hq, Hkv, Nq, Nk, d, causal)
     (1, 1, 1, 1, 1, 64, False),
