@@ -185,17 +185,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 fragment reads
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
             }
-            const bool need_mask = key0 + T::BN > kv_end || (CAUSAL && key0 + T::BN > qw + off);
+            // Whether this block needs the mask is the same for the whole wave;
+            // taken through readfirstlane so that it is one scalar branch around
+            // two copies of the loop (as a per-lane condition the compiler
+            // guards every element with its own exec-masked branch).
+            const bool need_mask = __builtin_amdgcn_readfirstlane(
+                (int)(key0 + T::BN > kv_end || (CAUSAL && key0 + T::BN > qw + off)));
+            auto form_ds = [&](auto masked) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float p = exp2_fast(__builtin_fmaf(s[i], sl2, -lse2));
-                if (need_mask) {
-                    const int key = key0 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                    const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
-                    p = ok ? p : 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    float p = exp2_fast(__builtin_fmaf(s[i], sl2, -lse2));
+                    if constexpr (decltype(masked)::value) {
+                        const int key = key0 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                        const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
+                        p = ok ? p : 0.f;
+                    }
+                    s[i] = p * (dp[i] - dlt);  // dS^T
                 }
-                s[i] = p * (dp[i] - dlt);  // dS^T
-            }
+            };
+            if (need_mask) form_ds(std::true_type{});
+            else form_ds(std::false_type{});
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 db;
@@ -367,25 +376,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 fragment reads
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
             }
-            const bool need_mask = kw + 32 > Nk || q0 + T::BQ > Nq || (CAUSAL && kw + 31 > q0 + off);
+            // one scalar branch around two copies of the loop (see the dQ kernel)
+            const bool need_mask = __builtin_amdgcn_readfirstlane(
+                (int)(kw + 32 > Nk || q0 + T::BQ > Nq || (CAUSAL && kw + 31 > q0 + off)));
+            auto form_p_ds = [&](auto masked) {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int r0 = gq * 8 + hf * 4;   // query rows r0..r0+3 of this step
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + r0);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int r0 = gq * 8 + hf * 4;   // query rows r0..r0+3 of this step
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + r0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = gq * 4 + r;
-                    float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -l4[r]));
-                    if (need_mask) {
-                        const int qi = q0 + r0 + r;
-                        const bool ok = kj < Nk && qi < Nq && (!CAUSAL || kj <= qi + off);
-                        p = ok ? p : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = gq * 4 + r;
+                        float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -l4[r]));
+                        if constexpr (decltype(masked)::value) {
+                            const int qi = q0 + r0 + r;
+                            const bool ok = kj < Nk && qi < Nq && (!CAUSAL || kj <= qi + off);
+                            p = ok ? p : 0.f;
+                        }
+                        sc[i] = p;
+                        dp[i] = p * (dp[i] - d4[r]);   // dS
                     }
-                    sc[i] = p;
-                    dp[i] = p * (dp[i] - d4[r]);   // dS
                 }
-            }
+            };
+            if (need_mask) form_p_ds(std::true_type{});
+            else form_p_ds(std::false_type{});
             // dV^T += dO^T P and dK^T += Q^T dS, transposing reads of the same tiles
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
