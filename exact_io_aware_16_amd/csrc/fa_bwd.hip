@@ -237,6 +237,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // 3. dK, dV, key owner
 // ---------------------------------------------------------------------------
+// dK/dV loop software-pipelined over query steps (1) or step by step (0);
+// DKV_ILV > 0 interleaves that many vector instructions after each MFMA
+#ifndef DKV_PIPE
+#define DKV_PIPE 1
+#endif
+#ifndef DKV_ILV
+#define DKV_ILV 4
+#endif
+
 template <int D>
 struct DkvTile {
     static constexpr int BK = 128;                 // keys per workgroup (4 waves x 32)
@@ -418,10 +427,139 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             }
         }
     };
+    // d = 128 only: at d = 64 the second S/dP buffer would halve the waves per SIMD
+    constexpr bool kPipe = DKV_PIPE && D >= 128;
+    if constexpr (kPipe) {
+    // Software-pipelined over steps: iteration stp forms P and dS of step stp
+    // and, in the same basic block, issues the S and dP products of step
+    // stp + 1 (independent of them), so the matrix cores run under the
+    // exponentials; then the dV and dK products of step stp.  S and dP are
+    // double-buffered; the ring still holds three steps (stp, stp + 1 read;
+    // stp + 2 loading).  Steps that a wave does not see (causal) or past the
+    // end still get their S/dP computed from valid (clamped) data and the
+    // result is never used.
+    static_assert(T::NS == 3, "the pipelined loop reads two ring stages while a third loads");
+    auto sdp = [&](auto slc, f32x16& sc, f32x16& dp) {
+        constexpr int slot = decltype(slc)::value;
+        const uint16_t* sQ = smem + slot * T::STAGE;
+        const uint16_t* sdO = sQ + T::TILE;
+        sc = zero16();
+        dp = zero16();
+#pragma unroll
+        for (int k0 = 0; k0 < D / 16; k0 += 4) {
+            bf16x8 qa[4], da[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                qa[kk] = frag_rows_swz<D>(sQ, 0, (k0 + kk) * 16, lane);
+                da[kk] = frag_rows_swz<D>(sdO, 0, (k0 + kk) * 16, lane);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                sc = mfma32x32x16(qa[kk], kf[k0 + kk], sc);
+                dp = mfma32x32x16(da[kk], vf[k0 + kk], dp);
+            }
+        }
+    };
+    auto active = [&](int stp) {
+        size_t base_unused;
+        int q0;
+        step_rows(stp, base_unused, q0);
+        return q0 + T::BQ > wave_q_begin && kw < Nk;
+    };
+    f32x16 scb[2], dpb[2];
+    if (total > 0) {
+        // step 0's loads are done once only step 1's may still fly
+        wait_vmcnt<T::LPS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        sdp(std::integral_constant<int, 0>{}, scb[0], dpb[0]);
+    }
+    auto iteration = [&](int stp, auto u) {
+        constexpr int U = decltype(u)::value;
+        constexpr int cur = U % 3, nxt = (U + 1) % 3, bc = U % 2, bn = 1 - U % 2;
+        // step stp + 1's loads (the only ones in flight) are done
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(stp + 2, (U + 2) % 3);
+        auto next = [&]() { sdp(std::integral_constant<int, nxt>{}, scb[bn], dpb[bn]); };
+        if (!active(stp)) {
+            next();
+            return;
+        }
+        size_t base_unused;
+        int q0;
+        step_rows(stp, base_unused, q0);
+        const uint16_t* sQ = smem + cur * T::STAGE;
+        const uint16_t* sdO = sQ + T::TILE;
+        const float* sL = reinterpret_cast<const float*>(sdO + T::TILE);
+        const float* sD = sL + T::BQ;
+        f32x16& sc = scb[bc];
+        f32x16& dp = dpb[bc];
+        const bool need_mask = __builtin_amdgcn_readfirstlane(
+            (int)(kw + 32 > Nk || q0 + T::BQ > Nq || (CAUSAL && kw + 31 > q0 + off)));
+        auto form_p_ds = [&](auto masked) {
+            next();
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int r0 = gq * 8 + hf * 4;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + r0);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = gq * 4 + r;
+                    float p = exp2_fast(__builtin_fmaf(sc[i], sl2, -l4[r]));
+                    if constexpr (decltype(masked)::value) {
+                        const int qi = q0 + r0 + r;
+                        const bool ok = kj < Nk && qi < Nq && (!CAUSAL || kj <= qi + off);
+                        p = ok ? p : 0.f;
+                    }
+                    sc[i] = p;
+                    dp[i] = p * (dp[i] - d4[r]);
+                }
+            }
+            if (DKV_ILV) {
+                // interleave: the next step's fragment reads, then each of its
+                // MFMAs followed by a few of this step's vector instructions
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, DKV_ILV, 0);
+                    }
+                }
+            }
+        };
+        if (need_mask) form_p_ds(std::true_type{});
+        else form_p_ds(std::false_type{});
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 pb, db;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[e] = (__bf16)sc[ks * 8 + e];
+                db[e] = (__bf16)dp[ks * 8 + e];
+            }
+#pragma unroll
+            for (int md = 0; md < D / 32; ++md) {
+                dv[md] = mfma32x32x16(frag_tr_swz<D>(sdO, ks * 16, md * 32, lane), pb, dv[md]);
+                dk[md] = mfma32x32x16(frag_tr_swz<D>(sQ, ks * 16, md * 32, lane), db, dk[md]);
+            }
+        }
+    };
+    for (int s0 = 0; s0 < total; s0 += 6) {
+        static_for<0, 6>([&](auto u) {
+            if (s0 + decltype(u)::value < total) iteration(s0 + decltype(u)::value, u);
+        });
+    }
+    } else {
     for (int s0 = 0; s0 < total; s0 += T::NS) {
         static_for<0, T::NS>([&](auto slc) {
             if (s0 + decltype(slc)::value < total) step(s0 + decltype(slc)::value, slc);
         });
+    }
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
