@@ -36,6 +36,26 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row sums of a P^T fragment on the matrix cores.  A B operand laid out for
+// the 32x32x16 MFMA (lane (n, h) = (l & 31, l >> 5) holding keys 8h..8h+7 of
+// query n) is, read as the B operand of a 16x16x32 MFMA, lane l holding rows
+// k = 8 (l >> 4) .. +7 of column l & 15: k-groups 0 and 2 belong to query
+// n = l & 15 and groups 1 and 3 to query n + 16.  With this A operand (row 0
+// selects groups 0 and 2, row 1 groups 1 and 3, every other entry 0), D[0][j]
+// is the sum over the fragment's 16 keys for query j and D[1][j] for query
+// j + 16; both sit in lane j (elements 0 and 1) of the 16x16 result.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+    const bool one = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (__bf16)(one ? 1.f : 0.f);
+    return a;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

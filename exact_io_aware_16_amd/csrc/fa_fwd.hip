@@ -64,6 +64,14 @@
 #ifndef RING_WPE64
 #define RING_WPE64 2
 #endif
+// softmax row sums on the matrix cores (rowsum_selector) instead of vector adds
+#ifndef RING_LSUM64
+#define RING_LSUM64 1
+#endif
+#ifndef RING_LSUM128
+#define RING_LSUM128 0
+#endif
+
 namespace fa {
 
 // Lazy rescaling threshold (log2 units): the running max is only raised when
@@ -164,6 +172,13 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
         m_run[nt] = kNegInf;
         l_run[nt] = 0.f;
     }
+    // row sums on the matrix cores: lacc[nt][0] / [1] of lane j < 16 hold the
+    // running sums of queries j and j + 16 of column tile nt
+    constexpr bool kMfmaSum = (D == 64 && RING_LSUM64) || (D == 128 && RING_LSUM128);
+    f32x4 lacc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 sel = rowsum_selector(lane);
 
     // prologue: blocks 0 .. S-2 (always S-1 stages issued, so the wait count is static)
 #pragma unroll
@@ -245,7 +260,14 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                 for (int nt = 0; nt < NT; ++nt) {
                     const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
                     const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
-                    l_run[nt] *= corr;
+                    if constexpr (kMfmaSum) {
+                        const float corr_hi = __int_as_float(
+                            __builtin_amdgcn_ds_bpermute(((lane + 16) & 63) << 2, __float_as_int(corr)));
+                        lacc[nt][0] *= corr;
+                        lacc[nt][1] *= corr_hi;
+                    } else {
+                        l_run[nt] *= corr;
+                    }
 #pragma unroll
                     for (int md = 0; md < D / 32; ++md)
 #pragma unroll
@@ -278,7 +300,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                         pb[nt][mt * 2 + (i >> 3)][i & 7] = (__bf16)p0;
                         pb[nt][mt * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)p1;
                     }
-                l_run[nt] += ps0 + ps1;
+                if constexpr (!kMfmaSum) l_run[nt] += ps0 + ps1;
             }
             // ---- O^T += V^T P^T -------------------------------------------------------------
 #pragma unroll
@@ -291,6 +313,10 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                 for (int md = 0; md < D / 32; ++md)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) ot[nt][md] = mfma32x32x16(va[md], pb[nt][ks], ot[nt][md]);
+                if constexpr (kMfmaSum) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma16x16x32(sel, pb[nt][ks], lacc[nt]);
+                }
             }
         }
     };
@@ -305,7 +331,15 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int qi = qw + nt * 32 + n;
-        const float l_tot = pair_sum(l_run[nt]);
+        float l_tot;
+        if constexpr (kMfmaSum) {
+            // query n's sum sits in lane n & 15, element n >> 4
+            const float a0 = __int_as_float(__builtin_amdgcn_ds_bpermute((n & 15) << 2, __float_as_int(lacc[nt][0])));
+            const float a1 = __int_as_float(__builtin_amdgcn_ds_bpermute((n & 15) << 2, __float_as_int(lacc[nt][1])));
+            l_tot = n < 16 ? a0 : a1;
+        } else {
+            l_tot = pair_sum(l_run[nt]);
+        }
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (qi < Nq) {
             uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
