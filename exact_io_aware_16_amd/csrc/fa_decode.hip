@@ -104,8 +104,9 @@ __device__ __forceinline__ void wait_stages(int r) {
 // ---------------------------------------------------------------------------
 // Stream-K variant.  The key range of every (sequence, K/V head, head tile)
 // row is cut into 32-key stages and all stages of all rows are laid end to
-// end; wave w of G takes the contiguous range [w S / G, (w+1) S / G) of the S
-// stages, so every wave streams the same number of bytes whatever the mix of
+// end; wave w of G takes a contiguous range of the S stages (dec_range_start:
+// equal shares, or a set skew between the XCDs of a pair), so the waves stream
+// the same number of bytes (or the set ratio) whatever the mix of
 // sequence lengths, and its ring of DS stages runs across row boundaries
 // without draining.  A stage holds 32 keys of K and V and the row's query
 // rows (dense, XOR-swizzled), all brought in by direct-to-LDS loads DS-1
@@ -115,6 +116,31 @@ __device__ __forceinline__ void wait_stages(int r) {
 // and there are at most rows + G of them.  Wave 0 also writes the prefix sums
 // of stages per sequence, from which the combine finds each row's waves.
 // ---------------------------------------------------------------------------
+// Share of the stages taken by the wave on the even XCD of each pair, in 64ths
+// (measured on MI355X: waves on odd XCDs stream 10-12% slower; 35/64 was
+// fastest, +2-3% over an even split).
+#ifndef DEC_EVEN64
+#define DEC_EVEN64 35
+#endif
+
+// Start of wave w's range of the S stages (w = G gives S).  Waves go in pairs
+// (2p, 2p+1), which the dispatcher places on an even and an odd XCD (one-wave
+// workgroup w runs on XCD w mod 8); pair p covers [p S / (G/2), (p+1) S / (G/2))
+// and its even wave the first DEC_EVEN64/64 of that.  G is even.
+__device__ __forceinline__ long long dec_range_start(int w, long long S, int G) {
+    const int gp = G >> 1, p = w >> 1;
+    const long long a = (long long)p * S / gp;
+    if ((w & 1) == 0) return a;
+    const long long e = (long long)(p + 1) * S / gp;
+    return a + (e - a) * DEC_EVEN64 / 64;
+}
+// the wave whose range holds stage st (0 <= st < S)
+__device__ __forceinline__ int dec_wave_of(long long st, long long S, int G) {
+    const int gp = G >> 1;
+    const int p = (int)(((st + 1) * gp - 1) / S);
+    return 2 * p + (st >= dec_range_start(2 * p + 1, S, G) ? 1 : 0);
+}
+
 template <int D, int DS, int QR>
 struct StreamTile {
     static constexpr int BK = 32;                    // keys per stage
@@ -176,8 +202,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
     }
     S = __builtin_amdgcn_readfirstlane(S);
     if (w == 0 && lane == 0) meta[B] = S;
-    const int s0 = (int)((long long)w * S / G);
-    const int s1 = (int)((long long)(w + 1) * S / G);
+    const int s0 = (int)dec_range_start(w, S, G);
+    const int s1 = (int)dec_range_start(w + 1, S, G);
     const int total = s1 - s0;
     if (total <= 0) return;
 
@@ -372,7 +398,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
 
 // Merge the partials of each (sequence, query head): the row's stages
 // [P, P + nb) were covered by waves wave_of(P) .. wave_of(P + nb - 1), where
-// wave w owns [w S / G, (w+1) S / G); waves with an empty range wrote nothing.
+// wave w owns [dec_range_start(w), dec_range_start(w + 1)); waves with an
+// empty range wrote nothing.
 template <int D>
 __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const int* __restrict__ meta,
@@ -393,8 +420,8 @@ __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
     const long long S = meta[B];
     const int r = b * HK + hk * nht + ht;
     const long long P = meta[b] + (long long)(hk * nht + ht) * nb;
-    auto wave_of = [&](long long st) { return (int)(((st + 1) * G - 1) / S); };
-    auto start_of = [&](int wv) { return (long long)wv * S / G; };
+    auto wave_of = [&](long long st) { return dec_wave_of(st, S, G); };
+    auto start_of = [&](int wv) { return dec_range_start(wv, S, G); };
     const int wf = wave_of(P), wl = wave_of(P + nb - 1);
     // The pieces' logsumexps are fetched together (one per thread) into LDS,
     // a chunk at a time, and merged with a running maximum, so the loads of
@@ -450,7 +477,7 @@ static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
         return e;
     // as many one-wave workgroups as the LDS of all CUs holds at once
     const int per_cu = std::max(1, std::min(8, lds / T::LDS_BYTES));
-    const int G = std::max(1, std::min(kDecodeMaxWaves, ncu * per_cu));
+    const int G = std::max(2, std::min(kDecodeMaxWaves, ncu * per_cu) & ~1);   // even (pairs)
     hipLaunchKernelGGL(kern, dim3(G), dim3(64), T::LDS_BYTES, (hipStream_t)a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o, a.part_lse, a.meta, a.B,
                        a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e);
