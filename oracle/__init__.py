@@ -12,6 +12,7 @@ from .attention import (  # noqa: F401
     online_softmax_stats,
     ref_bwd,
     ref_decode,
+    ref_decode_chunk,
     ref_fwd,
     ref_fwd_rows,
     ref_probs,

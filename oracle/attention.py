@@ -25,6 +25,10 @@ Sources (web pages; cited by title and section):
          Chính", item 2 (recomputation): the backward pass rebuilds P from Q, K, V
          instead of storing it.  The oracle's backward instead keeps its
          materialised P; it is the plain gradient of the forward definition.
+* [SPEC] handsonai.io, "DL101 chapter 9", section 1.2 "Speculative Decoding":
+         the large model checks a run of drafted tokens in one pass, each of
+         them under the rule of [KV] (attending to the keys up to its own
+         position).
 * [EX]   same glossary, section "Flash Attention Vs các kỹ Thuật Khác", and
          aiunderstanding.org "FlashAttention", section "Wawasan Teknis": the
          result is the same as standard attention, not an approximation.
@@ -41,6 +45,9 @@ design notes):
 * GQA head map: kv head = h // (Hq // Hkv); dK and dV of a kv head are summed
   over its query heads.
 * decode: the single query token sees every key j < len_b (no causal term).
+* chunk decode: the Nq new tokens are the last Nq of the len_b cached keys, so
+  causal token t sees keys j < len_b - (Nq - 1 - t); a token whose range is
+  empty (len_b < Nq - t) is a row with no valid key.
 
 Every function here is pinned by tests (closed forms, invariants, brute force,
 the printed tiled-vs-standard result of [TILE], and a library special case).
@@ -190,6 +197,27 @@ def ref_decode(q, k_cache, v_cache, seqlens, scale: float | None = None):
     """
     O, LSE = ref_fwd(q, k_cache, v_cache, causal=False, scale=scale, kv_lens=seqlens)
     return O, LSE[:, :, 0]
+
+
+def ref_decode_chunk(q, k_cache, v_cache, seqlens, causal: bool = True, scale: float | None = None):
+    """Nq new query tokens per (b, h) against the first seqlens[b] cached keys,
+    of which the last Nq are the new tokens' own ([SPEC], with [KV]'s rule).
+
+    causal: token t sees keys j < seqlens[b] - (Nq - 1 - t), i.e. the forward
+    over the sequence's own keys with bottom-right alignment; otherwise every
+    token sees keys j < seqlens[b].  q [B,Hq,Nq,d]; caches [B,Hkv,Nmax,d];
+    returns O [B,Hq,Nq,d], LSE [B,Hq,Nq].
+    """
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    Nmax = np.shape(k_cache)[2]
+    O = np.zeros((B, Hq, Nq, d))
+    LSE = np.full((B, Hq, Nq), NEG_INF)
+    for b in range(B):
+        n = max(0, min(Nmax, int(seqlens[b])))
+        O[b:b + 1], LSE[b:b + 1] = ref_fwd(q[b:b + 1], _f64(k_cache[b:b + 1, :, :n]), _f64(v_cache[b:b + 1, :, :n]),
+                                           causal=causal, scale=scale)
+    return O, LSE
 
 
 def ref_bwd(q, k, v, do, causal: bool = False, scale: float | None = None, kv_lens=None):

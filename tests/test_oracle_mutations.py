@@ -166,3 +166,43 @@ def test_backward_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(A, attr, fn)
     monkeypatch.setattr(oracle, attr, fn)
     assert _some_check_fails(_bwd_checks()), f"mutant {name} passed every pin"
+
+
+# chunk decode: plausible slips in the causal offset of the new tokens
+def _chunk_offset(shift, from_nmax=False):
+    def chunk(q, k, v, lens, causal, scale):
+        B, Hq, Nq, d = np.shape(q)
+        Nmax = np.shape(k)[2]
+        O = np.zeros((B, Hq, Nq, d)); L = np.full((B, Hq, Nq), -np.inf)
+        for b in range(B):
+            n = int(lens[b])
+            for t in range(Nq):
+                lim = (Nmax if from_nmax else n) - (Nq - 1 - t) + shift if causal else n
+                lim = max(0, min(n, lim))
+                Ot, Lt = oracle.ref_fwd(q[b:b + 1, :, t:t + 1], k[b:b + 1, :, :lim], v[b:b + 1, :, :lim], scale=scale)
+                O[b, :, t] = Ot[0, :, 0]; L[b, :, t] = Lt[0, :, 0]
+        return O, L
+    return chunk
+
+
+CHUNK_MUTANTS = {
+    "chunk_sees_next_token": _chunk_offset(+1),
+    "chunk_misses_own_token": _chunk_offset(-1),
+    "chunk_aligned_to_cache_capacity": _chunk_offset(0, from_nmax=True),
+}
+
+
+def _chunk_checks(chunk):
+    return [lambda: pins.check_chunk_brute_force(chunk), lambda: pins.check_chunk_rows_are_decodes(chunk),
+            lambda: pins.check_chunk_special_cases(chunk)]
+
+
+def test_unmutated_chunk_oracle_passes():
+    assert not _some_check_fails(_chunk_checks(pins.chunk_oracle))
+    # the mutant scaffold with no slip is the oracle itself
+    assert not _some_check_fails(_chunk_checks(_chunk_offset(0)))
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_MUTANTS))
+def test_chunk_mutant_is_caught(name):
+    assert _some_check_fails(_chunk_checks(CHUNK_MUTANTS[name])), f"mutant {name} passed every pin"

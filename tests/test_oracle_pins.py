@@ -413,3 +413,84 @@ def test_bwd_delta_identity():
     D1 = (P * dP).sum(-1)
     D2 = (do * O).sum(-1)
     assert np.abs(D1 - D2).max() <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# chunk decode (Nq new tokens against the cache; DL101 chapter 9, sections 1.1
+# and 1.2), checks parameterised by chunk(q, k, v, lens, causal, scale)
+# ---------------------------------------------------------------------------
+
+def check_chunk_brute_force(chunk):
+    """Per sequence: the pure-Python definition over its own len_b keys, causal
+    bottom-right aligned to len_b (token t sees keys j <= t + len_b - Nq)."""
+    ok = True
+    for seed, (B, Hq, Hkv, Nq, Nmax, d, lens) in enumerate([
+            (3, 4, 2, 3, 7, 3, [7, 5, 2]), (2, 2, 1, 4, 6, 2, [4, 0]), (1, 6, 3, 2, 5, 4, [1])]):
+        q, k, v = _rand(seed + 300, B, Hq, Nq, d), _rand(seed + 310, B, Hkv, Nmax, d), _rand(seed + 320, B, Hkv, Nmax, d)
+        for causal in (True, False):
+            O, L = chunk(q, k, v, np.array(lens), causal, 0.6)
+            for b in range(B):
+                n = lens[b]
+                Ob, Lb = brute_attention(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], causal, 0.6)
+                ok &= np.allclose(O[b], Ob[0], atol=1e-12, rtol=0) and np.allclose(L[b], Lb[0], atol=1e-12, rtol=0)
+    return bool(ok)
+
+
+def check_chunk_rows_are_decodes(chunk):
+    """Token t of a causal chunk is a one-token decode with the cache cut to
+    len_b - (Nq - 1 - t) keys; without causal, with all len_b keys."""
+    B, Hq, Hkv, Nq, Nmax, d = 3, 8, 2, 5, 40, 8
+    q, k, v = _rand(401, B, Hq, Nq, d), _rand(402, B, Hkv, Nmax, d), _rand(403, B, Hkv, Nmax, d)
+    lens = np.array([40, 17, 3])
+    Oc, Lc = chunk(q, k, v, lens, True, 0.3)
+    On, Ln = chunk(q, k, v, lens, False, 0.3)
+    ok = True
+    for t in range(Nq):
+        cut = np.maximum(lens - (Nq - 1 - t), 0)
+        Od, Ld = oracle.ref_decode(q[:, :, t:t + 1], k, v, cut, scale=0.3)
+        fin = np.isfinite(Ld)
+        ok &= np.abs(Oc[:, :, t] - Od[:, :, 0]).max() <= 1e-13 and np.array_equal(np.isneginf(Lc[:, :, t]), ~fin)
+        ok &= np.abs(Lc[:, :, t][fin] - Ld[fin]).max() <= 1e-13
+        Od, Ld = oracle.ref_decode(q[:, :, t:t + 1], k, v, lens, scale=0.3)
+        ok &= np.abs(On[:, :, t] - Od[:, :, 0]).max() <= 1e-13 and np.abs(Ln[:, :, t] - Ld).max() <= 1e-13
+    return bool(ok)
+
+
+def check_chunk_special_cases(chunk):
+    """Nq = 1 is decode; a chunk longer than its sequence leaves the first
+    tokens without keys (O = 0, LSE = -inf); keys past len_b never matter."""
+    ok = True
+    q, k, v = _rand(501, 2, 4, 1, 8), _rand(502, 2, 2, 30, 8), _rand(503, 2, 2, 30, 8)
+    lens = np.array([30, 9])
+    O, L = chunk(q, k, v, lens, True, 0.4)
+    Od, Ld = oracle.ref_decode(q, k, v, lens, scale=0.4)
+    ok &= np.abs(O - Od).max() <= 1e-14 and np.abs(L[:, :, 0] - Ld).max() <= 1e-14
+    q = _rand(504, 2, 4, 6, 8)
+    lens = np.array([4, 30])
+    O, L = chunk(q, k, v, lens, True, 0.4)
+    ok &= np.all(O[0, :, :2] == 0) and np.all(np.isneginf(L[0, :, :2])) and np.all(np.isfinite(L[0, :, 2:]))
+    # token 2 of sequence 0 sees exactly key 0: O = V_0, LSE = scale q.k_0
+    ok &= np.allclose(O[0, :, 2], np.repeat(v[0, :, 0], 2, axis=0), atol=1e-14)
+    ok &= np.allclose(L[0, :, 2], 0.4 * np.einsum("hd,hd->h", q[0, :, 2], np.repeat(k[0, :, 0], 2, axis=0)), atol=1e-13)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 4:] = np.inf
+    v2[0, :, 4:] = np.nan
+    O2, L2 = chunk(q, k2, v2, lens, True, 0.4)
+    ok &= np.array_equal(O2, O) and np.array_equal(L2, L)
+    return bool(ok)
+
+
+def chunk_oracle(q, k, v, lens, causal, scale):
+    return oracle.ref_decode_chunk(q, k, v, lens, causal=causal, scale=scale)
+
+
+def test_decode_chunk_brute_force():
+    assert check_chunk_brute_force(chunk_oracle)
+
+
+def test_decode_chunk_rows_are_decodes():
+    assert check_chunk_rows_are_decodes(chunk_oracle)
+
+
+def test_decode_chunk_special_cases():
+    assert check_chunk_special_cases(chunk_oracle)
