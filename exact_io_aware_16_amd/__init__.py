@@ -7,11 +7,13 @@ Every step of the computation runs in the HIP kernels of ``libfa.so``; there is
 no fallback of any kind.  PyTorch only provides device memory and streams.
 
 Low-level entry points mirror the C names (``fa_fwd``, ``fa_bwd``,
-``fa_decode``, ``fa_bwd_workspace_bytes``, ``fa_decode_workspace_bytes``) and
-write into caller-provided tensors; ``prepare_fwd`` / ``prepare_bwd`` /
-``prepare_decode`` do the checks and marshalling once and return a callable
-that only launches (for tight loops).  ``fwd``, ``bwd`` and ``decode`` allocate
-their outputs with torch and call them.
+``fa_decode``, ``fa_decode_chunk``, ``fa_bwd_workspace_bytes``,
+``fa_decode_workspace_bytes``, ``fa_decode_chunk_workspace_bytes``) and write
+into caller-provided tensors; ``prepare_fwd`` / ``prepare_bwd`` /
+``prepare_decode`` / ``prepare_decode_chunk`` do the checks and marshalling
+once and return a callable that only launches (for tight loops).  ``fwd``,
+``bwd``, ``decode`` and ``decode_chunk`` allocate their outputs with torch and
+call them.
 """
 from __future__ import annotations
 
@@ -57,6 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode_chunk_workspace_bytes.restype = sz
+    lib.fa_decode_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_chunk.restype = i
+    lib.fa_decode_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -113,6 +119,10 @@ def fa_bwd_workspace_bytes(B, Hq, Nq, d) -> int:
 
 def fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d) -> int:
     return load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)
+
+
+def fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d) -> int:
+    return load_library().fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d)
 
 
 def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
@@ -175,6 +185,29 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, strea
     prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=scale, stream=stream)()
 
 
+def prepare_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=True, scale=None, stream=None):
+    """fa_decode_chunk's arguments checked and marshalled once (see prepare_fwd)."""
+    _dev(q, k_cache, v_cache, seqlens, o, lse, workspace)
+    torch = _torch()
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nmax, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nmax, d,
+            _dtype_code(q), scale, int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return lambda: _check(lib.fa_decode_chunk(*args))
+
+
+def fa_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=True, scale=None, stream=None):
+    """Nq new tokens per head against the first seqlens[b] cached keys (the last
+    Nq of which are theirs); causal: token t sees keys < seqlens[b] - (Nq-1-t)."""
+    prepare_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=causal, scale=scale,
+                         stream=stream)()
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (outputs allocated by torch, computed by libfa)
 # ---------------------------------------------------------------------------
@@ -215,4 +248,22 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, workspace=None, stream=None
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     ws = decode_workspace(q, k_cache) if workspace is None else workspace
     fa_decode(q, k_cache, v_cache, seqlens, o, lse, ws, scale=scale, stream=stream)
+    return o, lse
+
+
+def decode_chunk_workspace(q, k_cache):
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nmax, _ = k_cache.shape
+    return torch.empty(max(1, fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d)), dtype=torch.uint8,
+                       device=q.device)
+
+
+def decode_chunk(q, k_cache, v_cache, seqlens, causal=True, scale=None, workspace=None, stream=None):
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ws = decode_chunk_workspace(q, k_cache) if workspace is None else workspace
+    fa_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, ws, causal=causal, scale=scale, stream=stream)
     return o, lse

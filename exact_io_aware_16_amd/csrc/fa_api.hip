@@ -16,6 +16,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 31;
 
 bool too_big(int64_t a, int64_t b, int64_t c, int64_t d) { return a * b * c * d >= kMaxElems; }
 
+// most new tokens per fa_decode_chunk call
+constexpr int kMaxChunk = 64;
+
 fa_status_t check_scale(float scale) {
     return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_ARG;
 }
@@ -112,6 +115,43 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, c
     }
     fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nmax, d, scale, nullptr, nullptr,
                      nullptr, stream};
+    float* ws = static_cast<float*>(workspace);
+    fa::decode_workspace_layout(a, ws);
+    return from_hip(fa::launch_decode_bf16(a));
+}
+
+size_t fa_decode_chunk_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nmax, int d) {
+    if (Nq < 1 || Nq > kMaxChunk || B < 1 || Hq < 1 || Hkv < 1 || Nmax < 1 || d < 1 || Hq % Hkv != 0) return 0;
+    return fa::decode_workspace_bytes(B, Hq * Nq, Hkv, Nmax, d);
+}
+
+fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_cache, const int* seqlens, void* o,
+                            float* lse, int B, int Hq, int Hkv, int Nq, int Nmax, int d, fa_dtype_t dtype,
+                            float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nmax < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0 || Nq > kMaxChunk) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, Nq, d) || too_big(B, Hkv, Nmax, d)) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!workspace || workspace_bytes < fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d))
+        return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(seqlens) || !aligned16(o) ||
+        !aligned4(lse) || !aligned16(workspace))
+        return FA_ERR_ARG;
+    if (dtype == FA_F32) {
+        // float32: the forward kernel with per-sequence key limits; its causal
+        // offset is taken from each sequence's own length
+        fa::FwdArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, Nmax, d, scale, causal ? 1 : 0, stream};
+        return from_hip(fa::launch_fwd_f32(a, seqlens));
+    }
+    // bfloat16: the streaming decode over the Hq * Nq (head, token) rows; the
+    // Nq rows of a head are consecutive in q, o and lse, so a group of K/V
+    // head hk is its g * Nq consecutive rows
+    fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq * Nq, Hkv, Nmax, d, scale, nullptr, nullptr,
+                     nullptr, stream};
+    a.cq = causal ? Nq : 1;
     float* ws = static_cast<float*>(workspace);
     fa::decode_workspace_layout(a, ws);
     return from_hip(fa::launch_decode_bf16(a));

@@ -174,7 +174,7 @@ template <int D, int DS, int QR>
 __global__ __launch_bounds__(64) void decode_stream_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int* __restrict__ meta, int B, int Hq, int Hkv, int Nmax, int nht, int G, float sl2) {
+    int* __restrict__ meta, int B, int Hq, int Hkv, int Nmax, int nht, int G, float sl2, int cq) {
     using T = StreamTile<D, DS, QR>;
     static_assert(DS <= 5, "wait_stages covers at most five stages");
     extern __shared__ __align__(16) uint16_t smem[];
@@ -311,6 +311,10 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
         const uint16_t* sQ = sV + T::TILE;
         const int key0 = cc.j * T::BK;
         const int k_end = cc.len;
+        // Causal chunk (cq new tokens per query head, cq = 1 otherwise): row
+        // rho of the group is token rho % cq, which sees the keys below
+        // k_end - (cq - 1 - rho % cq).  Lane n holds row 32 ht + n.
+        const int row_lim = k_end - (cq - 1) + min(cc.ri % nht * 32 + n, g - 1) % cq;
         if (cc.j == 0 || k == 0) {
             // Q^T operand of the row: lane (n, hf) takes query row min(n, QR-1)
             const int qr = min(n, QR - 1);
@@ -324,11 +328,11 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
         f32x16 sc = zero16();
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) sc = mfma32x32x16(kf[kk], qf[kk], sc);
-        if (key0 + T::BK > k_end) {
+        if (key0 + T::BK > k_end - (cq - 1)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = key0 + (i >> 2) * 8 + hf * 4 + (i & 3);
-                sc[i] = key < k_end ? sc[i] : kNegInf;
+                sc[i] = key < row_lim ? sc[i] : kNegInf;
             }
         }
         float m0 = kNegInf, m1 = kNegInf;
@@ -450,13 +454,16 @@ __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
             // (unwritten) contents are discarded by the select
             const float l = s_lse[t];
             const float v = part_o[((size_t)(r + c0 + t) * TR + hi) * D + dcol];
-            const float wt = exp2_fast((l - M) * kLog2e);
+            // a piece that saw no key of this row (lse = -inf) weighs 0, also
+            // while every piece so far is empty (M = -inf)
+            const float wt = l == kNegInf ? 0.f : exp2_fast((l - M) * kLog2e);
             L += wt;
             acc += l == kNegInf ? 0.f : wt * v;
         }
     }
-    orow[dcol] = f32_to_bf16_bits(acc / L);
-    if (dcol == 0) LSE[b * Hq + hq] = M + log2_fast(L) * kLn2;
+    // a row that sees no key at all (a causal chunk longer than its sequence): O = 0, LSE = -inf
+    orow[dcol] = f32_to_bf16_bits(L > 0.f ? acc / L : 0.f);
+    if (dcol == 0) LSE[b * Hq + hq] = L > 0.f ? M + log2_fast(L) * kLn2 : kNegInf;
 }
 
 #ifndef DEC_STAGES
@@ -480,7 +487,7 @@ static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
     const int G = std::max(2, std::min(kDecodeMaxWaves, ncu * per_cu) & ~1);   // even (pairs)
     hipLaunchKernelGGL(kern, dim3(G), dim3(64), T::LDS_BYTES, (hipStream_t)a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o, a.part_lse, a.meta, a.B,
-                       a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e);
+                       a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e, a.cq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_stream_combine_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, (hipStream_t)a.stream,
                        a.part_o, a.part_lse, a.meta, a.seqlens, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nmax,

@@ -391,10 +391,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const int tid = threadIdx.x;
     const int row = tid >> 2, part = tid & 3;
     const int qi = blockIdx.x * 64 + row;
-    const int off = Nk - Nq;
 
     int kv_end = Nk;
     if (kv_lens) kv_end = max(0, min(Nk, kv_lens[b]));
+    // causal is bottom-right aligned to the sequence's own length
+    const int off = kv_end - Nq;
     int wg_end = kv_end;
     if (causal) wg_end = min(kv_end, blockIdx.x * 64 + 64 + off);
 

@@ -50,6 +50,10 @@ struct DecodeArgs {
     float* part_lse;  // workspace: [slots][rows per slot] float32
     int* meta;        // workspace: [B + 1] int32 (stage prefix per sequence)
     void* stream;
+    // Query rows per head forming one causal chunk (the last cq rows of the
+    // sequence, bottom-right aligned): Hq then counts (head, token) rows, cq
+    // consecutive ones per head.  1 for plain decode and non-causal chunks.
+    int cq = 1;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);

@@ -125,6 +125,35 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       fa_dtype_t dtype, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace fa_decode_chunk needs: the same partial results
+ * as fa_decode over Hq * Nq query rows.  0 for shapes fa_decode_chunk would
+ * reject. */
+size_t fa_decode_chunk_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nmax, int d);
+
+/*
+ * Chunk decode: Nq new query tokens per (b, h) against a KV cache that already
+ * holds their keys and values, as when a large model checks several drafted
+ * tokens in one pass or a prompt is prefilled in chunks (DL101 chapter 9,
+ * section 1.2 Speculative Decoding, with the rule of section 1.1: token t
+ * attends to the keys up to and including its own position).
+ *   q [B,Hq,Nq,d]; k_cache/v_cache [B,Hkv,Nmax,d]; seqlens [B] int32 on the
+ *   DEVICE (clamped to [0, Nmax]): sequence b's cache holds seqlens[b] keys,
+ *   the last Nq of which belong to the new tokens.  o [B,Hq,Nq,d] in dtype;
+ *   lse [B,Hq,Nq] float32.
+ *   causal != 0: token t (0 <= t < Nq) sees keys j < seqlens[b] - (Nq - 1 - t),
+ *   i.e. bottom-right aligned to the sequence's own length; a token whose
+ *   range is empty (seqlens[b] < Nq - t) gets o = 0 and lse = -inf.
+ *   causal == 0: every token sees keys j < seqlens[b].
+ *   1 <= Nq <= 64; Nq == 1 is fa_decode.
+ *   workspace: device buffer of at least fa_decode_chunk_workspace_bytes(...)
+ *   bytes.  Other conventions as fa_decode.
+ */
+fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seqlens, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nmax, int d,
+                            fa_dtype_t dtype, float scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

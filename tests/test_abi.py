@@ -111,9 +111,27 @@ def test_decode_validation(lib):
     assert dec(wsb=need - 1) == 5
 
 
+def test_decode_chunk_validation(lib):
+    def chunk(seq=P, ws=P, wsb=1 << 26, d=128, Hq=32, Hkv=8, Nq=8, Nmax=1024, causal=1):
+        return lib.fa_decode_chunk(P, P, P, seq, P, P, 2, Hq, Hkv, Nq, Nmax, d, 1, 0.088, causal, ws, wsb, N)
+    assert chunk(seq=N) == 1
+    assert chunk(Hq=30, Hkv=8) == 2
+    assert chunk(Nq=0) == 2
+    assert chunk(Nq=65) == 2
+    assert chunk(Nmax=0) == 2
+    assert chunk(d=80) == 4
+    assert chunk(ws=N) == 5
+    need = lib.fa_decode_chunk_workspace_bytes(2, 32, 8, 8, 1024, 128)
+    assert need > 0 and chunk(wsb=need - 1) == 5
+    # one new token needs what decode needs; more tokens need more partial rows
+    assert lib.fa_decode_chunk_workspace_bytes(2, 32, 8, 1, 1024, 128) == lib.fa_decode_workspace_bytes(2, 32, 8, 1024, 128)
+    assert lib.fa_decode_chunk_workspace_bytes(2, 32, 8, 16, 1024, 128) > need
+    assert lib.fa_decode_chunk_workspace_bytes(2, 32, 8, 65, 1024, 128) == 0
+
+
 def test_binding_names_match_header():
-    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
-              "fa_abi_version"):
+    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_bwd_workspace_bytes",
+              "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes", "fa_abi_version"):
         assert callable(getattr(fa, n))
 
 
