@@ -54,7 +54,7 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
-    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode"], default=None,
+    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode", "decode_chunk"], default=None,
                     help="run only this row (for profiling one kernel); prints the row as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain 256 MiB device copies (known bytes) to scale rocprofv3 "
@@ -262,6 +262,37 @@ def row_decode(args, fa, W):
                     "warm = back-to-back launches; cold_after_writes = caches filled with dirty lines first"}
 
 
+def row_decode_chunk(args, fa, W):
+    """Chunk decode on the decode workload's cache: 8 new tokens per head
+    (causal to each sequence's length), as when a large model checks 8 drafted
+    tokens; bytes as decode (valid K/V once) plus the larger q, o and lse."""
+    import numpy as np
+    import torch
+    nq = 8
+    w = W.make_config(4, Nq=nq)
+    t = upload(w)
+    sl = torch.from_numpy(w.seqlens).to("cuda:0")
+    q, k, v = t["q"], t["k"], t["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, nq), dtype=torch.float32, device="cuda:0")
+    ws = fa.decode_chunk_workspace(q, k)
+    run = fa.prepare_decode_chunk(q, k, v, sl, o, lse, ws, causal=True, scale=w.scale)
+    valid = int(w.seqlens.astype(np.int64).sum())
+    nbytes = valid * w.Hkv * w.d * 2 * 2 + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
+    flops = 4 * w.Hq * w.d * sum(int(n) * nq - nq * (nq - 1) // 2 for n in w.seqlens)
+    n = max(10, args.steps // 2)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0")
+    flush.sum()
+    torch.cuda.synchronize()
+    tc, _ = time_launches(run, n, 2, before=lambda: flush.sum())
+    sc = stats(tc)
+    gbps = nbytes / (sc["median_us"] * 1e-6) / 1e9
+    return {"workload": "gqa_decode_chunk_B16_Hq32_Hkv8_Nq8_N32768_d128_bf16_causal", "valid_keys": valid,
+            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
+            "tflops": flops / (sc["median_us"] * 1e-6) / 1e12, "cold": sc,
+            "note": "caches emptied (by reading a 1 GiB buffer) before each launch"}
+
+
 def cpu_baseline(args, head, W):
     """The fp64 oracle on the host cores, on whole heads of the headline workload,
     until the CPU budget is spent; also checks the GPU's output on those heads."""
@@ -314,7 +345,8 @@ def main():
     fa.load_library()   # raises if libfa.so is not built: there is no other path
 
     if args.only:
-        fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode}[args.only]
+        fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode,
+              "decode_chunk": row_decode_chunk}[args.only]
         print(json.dumps({args.only: fn(args, fa, W)}), flush=True)
         return
 
@@ -338,6 +370,9 @@ def main():
         torch.cuda.empty_cache()
         log("row: GQA decode B16 Hq32 Hkv8 N32768 d128 bf16")
         rows["decode"] = row_decode(args, fa, W)
+        torch.cuda.empty_cache()
+        log("row: GQA chunk decode B16 Hq32 Hkv8 Nq8 N32768 d128 bf16")
+        rows["decode_chunk"] = row_decode_chunk(args, fa, W)
         torch.cuda.empty_cache()
     cpu = None
     if not args.headline_only and not args.no_cpu_baseline:
