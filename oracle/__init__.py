@@ -13,6 +13,8 @@ from .attention import (  # noqa: F401
     ref_bwd,
     ref_decode,
     ref_decode_chunk,
+    ref_decode_paged,
+    gather_pages,
     ref_fwd,
     ref_fwd_rows,
     ref_probs,

@@ -29,6 +29,10 @@ Sources (web pages; cited by title and section):
          the large model checks a run of drafted tokens in one pass, each of
          them under the rule of [KV] (attending to the keys up to its own
          position).
+* [PAGE] unite.ai "What is FlashAttention", section "Nguồn chính để nghiên cứu
+         FlashAttention": names vLLM's PagedAttention (a KV cache kept in
+         fixed-size pages reached through a per-sequence block table) as where
+         the method meets serving; the pages define nothing further.
 * [EX]   same glossary, section "Flash Attention Vs các kỹ Thuật Khác", and
          aiunderstanding.org "FlashAttention", section "Wawasan Teknis": the
          result is the same as standard attention, not an approximation.
@@ -45,6 +49,9 @@ design notes):
 * GQA head map: kv head = h // (Hq // Hkv); dK and dV of a kv head are summed
   over its query heads.
 * decode: the single query token sees every key j < len_b (no causal term).
+* paged cache: pool [num_pages, Hkv, page_size, d]; block_table[b, p] names the
+  physical page holding keys p*page_size .. (p+1)*page_size - 1 of sequence b;
+  the result is that of the contiguous cache those pages spell out.
 * chunk decode: the Nq new tokens are the last Nq of the len_b cached keys, so
   causal token t sees keys j < len_b - (Nq - 1 - t); a token whose range is
   empty (len_b < Nq - t) is a row with no valid key.
@@ -217,6 +224,38 @@ def ref_decode_chunk(q, k_cache, v_cache, seqlens, causal: bool = True, scale: f
         n = max(0, min(Nmax, int(seqlens[b])))
         O[b:b + 1], LSE[b:b + 1] = ref_fwd(q[b:b + 1], _f64(k_cache[b:b + 1, :, :n]), _f64(v_cache[b:b + 1, :, :n]),
                                            causal=causal, scale=scale)
+    return O, LSE
+
+
+def gather_pages(pages, block_table, b: int, n: int, page_size: int) -> np.ndarray:
+    """The first n keys of sequence b as a contiguous [Hkv, n, d] array ([PAGE]):
+    key j lives in physical page block_table[b, j // page_size], row j % page_size."""
+    pages = _f64(pages)
+    Hkv, d = pages.shape[1], pages.shape[3]
+    out = np.zeros((Hkv, n, d))
+    for j in range(n):
+        out[:, j] = pages[int(block_table[b, j // page_size]), :, j % page_size]
+    return out
+
+
+def ref_decode_paged(q, k_pages, v_pages, block_table, seqlens, page_size: int, causal: bool = True,
+                     scale: float | None = None):
+    """Chunk decode (ref_decode_chunk) against a paged cache ([PAGE]).
+
+    k_pages/v_pages [num_pages, Hkv, page_size, d]; block_table [B, max_pages]
+    int; seqlens [B] clamped to [0, max_pages * page_size].  q [B,Hq,Nq,d];
+    returns O [B,Hq,Nq,d], LSE [B,Hq,Nq].
+    """
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    cap = np.shape(block_table)[1] * page_size
+    O = np.zeros((B, Hq, Nq, d))
+    LSE = np.full((B, Hq, Nq), NEG_INF)
+    for b in range(B):
+        n = max(0, min(cap, int(seqlens[b])))
+        kb = gather_pages(k_pages, block_table, b, n, page_size)[None]
+        vb = gather_pages(v_pages, block_table, b, n, page_size)[None]
+        O[b:b + 1], LSE[b:b + 1] = ref_decode_chunk(q[b:b + 1], kb, vb, [n], causal=causal, scale=scale)
     return O, LSE
 
 

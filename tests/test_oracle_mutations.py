@@ -206,3 +206,64 @@ def test_unmutated_chunk_oracle_passes():
 @pytest.mark.parametrize("name", sorted(CHUNK_MUTANTS))
 def test_chunk_mutant_is_caught(name):
     assert _some_check_fails(_chunk_checks(CHUNK_MUTANTS[name])), f"mutant {name} passed every pin"
+
+
+# paged cache: plausible slips in the page lookup
+def _paged_with_gather(gather):
+    def paged(q, kp, vp, table, lens, P, causal, scale):
+        q = np.asarray(q, dtype=np.float64)
+        B, Hq, Nq, d = q.shape
+        O = np.zeros((B, Hq, Nq, d)); L = np.full((B, Hq, Nq), -np.inf)
+        for b in range(B):
+            n = max(0, min(np.shape(table)[1] * P, int(lens[b])))
+            kb, vb = gather(kp, table, b, n, P)[None], gather(vp, table, b, n, P)[None]
+            O[b:b + 1], L[b:b + 1] = oracle.ref_decode_chunk(q[b:b + 1], kb, vb, [n], causal=causal, scale=scale)
+        return O, L
+    return paged
+
+
+def _gather_row_page_swapped(pages, table, b, n, P):
+    pages = np.asarray(pages, dtype=np.float64)
+    out = np.zeros((pages.shape[1], n, pages.shape[3]))
+    for j in range(n):
+        out[:, j] = pages[int(table[b, min(j % P, table.shape[1] - 1)]), :, min(j // P, P - 1)]
+    return out
+
+
+def _gather_table_by_page_then_seq(pages, table, b, n, P):
+    pages = np.asarray(pages, dtype=np.float64)
+    flat = np.asarray(table).T.reshape(table.shape)   # rows read in the wrong order
+    out = np.zeros((pages.shape[1], n, pages.shape[3]))
+    for j in range(n):
+        out[:, j] = pages[int(flat[b, j // P]), :, j % P]
+    return out
+
+
+def _gather_first_page_only(pages, table, b, n, P):
+    pages = np.asarray(pages, dtype=np.float64)
+    out = np.zeros((pages.shape[1], n, pages.shape[3]))
+    for j in range(n):
+        out[:, j] = pages[int(table[b, 0]), :, j % P]
+    return out
+
+
+PAGED_MUTANTS = {
+    "page_and_row_swapped": _paged_with_gather(_gather_row_page_swapped),
+    "table_read_transposed": _paged_with_gather(_gather_table_by_page_then_seq),
+    "first_page_reused": _paged_with_gather(_gather_first_page_only),
+}
+
+
+def _paged_checks(paged):
+    return [lambda: pins.check_paged_contiguous_case(paged), lambda: pins.check_paged_brute_force(paged),
+            lambda: pins.check_paged_invariants(paged)]
+
+
+def test_unmutated_paged_oracle_passes():
+    assert not _some_check_fails(_paged_checks(pins.paged_oracle))
+    assert not _some_check_fails(_paged_checks(_paged_with_gather(oracle.gather_pages)))
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MUTANTS))
+def test_paged_mutant_is_caught(name):
+    assert _some_check_fails(_paged_checks(PAGED_MUTANTS[name])), f"mutant {name} passed every pin"

@@ -494,3 +494,99 @@ def test_decode_chunk_rows_are_decodes():
 
 def test_decode_chunk_special_cases():
     assert check_chunk_special_cases(chunk_oracle)
+
+
+# ---------------------------------------------------------------------------
+# paged cache (unite.ai "What is FlashAttention", sources section, naming
+# vLLM's PagedAttention), checks parameterised by
+# paged(q, k_pages, v_pages, table, lens, page_size, causal, scale)
+# ---------------------------------------------------------------------------
+
+def _pool_from_contiguous(k, page_size):
+    """[B, Hkv, max_pages*P, d] -> pool [B*max_pages, Hkv, P, d] with sequence b's
+    page p at physical index b*max_pages + p (a plain reshape)."""
+    B, Hkv, N, d = k.shape
+    mp = N // page_size
+    return k.reshape(B, Hkv, mp, page_size, d).transpose(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page_size, d)
+
+
+def check_paged_contiguous_case(paged):
+    """An identity block table over a reshaped contiguous cache is the chunk
+    decode of that cache (a case that reduces to the pinned chunk oracle)."""
+    ok = True
+    for seed, (B, Hq, Hkv, Nq, P, mp, d, lens) in enumerate([
+            (3, 8, 2, 1, 32, 4, 8, [128, 70, 0]), (2, 4, 1, 3, 16, 5, 4, [80, 2])]):
+        q = _rand(seed + 600, B, Hq, Nq, d)
+        k, v = _rand(seed + 610, B, Hkv, mp * P, d), _rand(seed + 620, B, Hkv, mp * P, d)
+        table = np.arange(B * mp).reshape(B, mp)
+        for causal in (True, False):
+            O, L = paged(q, _pool_from_contiguous(k, P), _pool_from_contiguous(v, P), table, np.array(lens), P,
+                         causal, 0.45)
+            Oc, Lc = oracle.ref_decode_chunk(q, k, v, np.array(lens), causal=causal, scale=0.45)
+            ok &= np.array_equal(O, Oc) and np.array_equal(L, Lc)
+    return bool(ok)
+
+
+def check_paged_brute_force(paged):
+    """Pure Python: key j of sequence b is row j % P of page table[b][j // P]."""
+    B, Hq, Hkv, Nq, P, npages, mp, d = 2, 4, 2, 2, 4, 7, 3, 3
+    q = _rand(630, B, Hq, Nq, d)
+    kp, vp = _rand(631, npages, Hkv, P, d), _rand(632, npages, Hkv, P, d)
+    table = np.array([[5, 0, 3], [6, 2, 1]])
+    lens = [11, 6]
+    O, L = paged(q, kp, vp, table, np.array(lens), P, True, 0.8)
+    ok = True
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(Nq):
+                keys = [j for j in range(lens[b]) if j <= lens[b] - Nq + t]
+                row = lambda x, j: [float(c) for c in x[table[b][j // P], h // g, j % P]]
+                s = {j: 0.8 * sum(a * c for a, c in zip(q[b, h, t], row(kp, j))) for j in keys}
+                mx = max(s.values())
+                den = sum(math.exp(s[j] - mx) for j in keys)
+                ref = [sum(math.exp(s[j] - mx) / den * row(vp, j)[c] for j in keys) for c in range(d)]
+                ok &= np.allclose(O[b, h, t], ref, atol=1e-12, rtol=0) and abs(L[b, h, t] - (mx + math.log(den))) < 1e-12
+    return bool(ok)
+
+
+def check_paged_invariants(paged):
+    """Renumbering the physical pages (and the table with them) changes nothing;
+    pages the table does not reach, and table entries past a sequence's last
+    page, never matter."""
+    B, Hq, Hkv, Nq, P, npages, mp, d = 3, 4, 2, 3, 32, 12, 3, 8
+    q = _rand(640, B, Hq, Nq, d)
+    kp, vp = _rand(641, npages, Hkv, P, d), _rand(642, npages, Hkv, P, d)
+    table = np.array([[3, 7, 1], [0, 11, 9], [4, 2, 8]])
+    lens = np.array([96, 40, 33])
+    O, L = paged(q, kp, vp, table, lens, P, True, 0.3)
+    perm = np.random.Generator(np.random.PCG64(643)).permutation(npages)   # physical page i -> perm[i]
+    kq, vq = np.empty_like(kp), np.empty_like(vp)
+    kq[perm], vq[perm] = kp, vp
+    O2, L2 = paged(q, kq, vq, perm[table], lens, P, True, 0.3)
+    ok = np.array_equal(O, O2) and np.array_equal(L, L2)
+    used = {int(table[b, p]) for b in range(B) for p in range(-(-int(lens[b]) // P))}
+    k3, v3, t3 = kp.copy(), vp.copy(), table.copy()
+    for i in range(npages):
+        if i not in used:
+            k3[i], v3[i] = np.inf, np.nan
+    t3[1, 2] = 5   # past sequence 1's last page (40 keys = 2 pages)
+    O3, L3 = paged(q, k3, v3, t3, lens, P, True, 0.3)
+    ok &= np.array_equal(O, O3) and np.array_equal(L, L3)
+    return bool(ok)
+
+
+def paged_oracle(q, kp, vp, table, lens, page_size, causal, scale):
+    return oracle.ref_decode_paged(q, kp, vp, table, lens, page_size, causal=causal, scale=scale)
+
+
+def test_paged_contiguous_case():
+    assert check_paged_contiguous_case(paged_oracle)
+
+
+def test_paged_brute_force():
+    assert check_paged_brute_force(paged_oracle)
+
+
+def test_paged_invariants():
+    assert check_paged_invariants(paged_oracle)
