@@ -7,12 +7,11 @@ Every step of the computation runs in the HIP kernels of ``libfa.so``; there is
 no fallback of any kind.  PyTorch only provides device memory and streams.
 
 Low-level entry points mirror the C names (``fa_fwd``, ``fa_bwd``,
-``fa_decode``, ``fa_decode_chunk``, ``fa_bwd_workspace_bytes``,
-``fa_decode_workspace_bytes``, ``fa_decode_chunk_workspace_bytes``) and write
-into caller-provided tensors; ``prepare_fwd`` / ``prepare_bwd`` /
-``prepare_decode`` / ``prepare_decode_chunk`` do the checks and marshalling
-once and return a callable that only launches (for tight loops).  ``fwd``,
-``bwd``, ``decode`` and ``decode_chunk`` allocate their outputs with torch and
+``fa_decode``, ``fa_decode_chunk``, ``fa_decode_paged`` and their
+``*_workspace_bytes``) and write into caller-provided tensors; the
+``prepare_*`` functions do the checks and marshalling once and return a
+callable that only launches (for tight loops).  ``fwd``, ``bwd``, ``decode``,
+``decode_chunk`` and ``decode_paged`` allocate their outputs with torch and
 call them.
 """
 from __future__ import annotations
@@ -63,6 +62,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_chunk.restype = i
     lib.fa_decode_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode_paged_workspace_bytes.restype = sz
+    lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_paged.restype = i
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -123,6 +126,10 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d) -> int:
 
 def fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d) -> int:
     return load_library().fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, Nmax, d)
+
+
+def fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, d) -> int:
+    return load_library().fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, d)
 
 
 def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
@@ -208,6 +215,33 @@ def fa_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=True
                          stream=stream)()
 
 
+def prepare_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, causal=True, scale=None,
+                         stream=None):
+    """fa_decode_paged's arguments checked and marshalled once (see prepare_fwd).
+    k_pages/v_pages [num_pages, Hkv, page_size, d]; block_table [B, max_pages] int32."""
+    _dev(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace)
+    torch = _torch()
+    if seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("seqlens and block_table must be int32")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    args = (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq,
+            Hkv, Nq, num_pages, page_size, max_pages, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return lambda: _check(lib.fa_decode_paged(*args))
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, causal=True, scale=None,
+                    stream=None):
+    """fa_decode_chunk against a paged cache: key j of sequence b is row
+    j % page_size of page block_table[b, j // page_size]."""
+    prepare_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, causal=causal, scale=scale,
+                         stream=stream)()
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (outputs allocated by torch, computed by libfa)
 # ---------------------------------------------------------------------------
@@ -266,4 +300,18 @@ def decode_chunk(q, k_cache, v_cache, seqlens, causal=True, scale=None, workspac
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     ws = decode_chunk_workspace(q, k_cache) if workspace is None else workspace
     fa_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, ws, causal=causal, scale=scale, stream=stream)
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, causal=True, scale=None, workspace=None, stream=None):
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv = k_pages.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, d)), dtype=torch.uint8,
+                                device=q.device)
+    fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, causal=causal, scale=scale,
+                    stream=stream)
     return o, lse

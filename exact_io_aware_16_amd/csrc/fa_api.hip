@@ -157,4 +157,42 @@ fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_ca
     return from_hip(fa::launch_decode_bf16(a));
 }
 
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d) {
+    return fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, 1, d);
+}
+
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                            const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int num_pages,
+                            int page_size, int max_pages, int d, fa_dtype_t dtype, float scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seqlens || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || num_pages < 1 || page_size < 1 || max_pages < 1 || d < 1)
+        return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0 || Nq > kMaxChunk) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, Nq, d) || too_big(num_pages, Hkv, page_size, d) || too_big(max_pages, page_size, 1, 1) ||
+        too_big(B, max_pages, 1, 1))
+        return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (page_size % 32 != 0) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!workspace || workspace_bytes < fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, d)) return FA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned4(block_table) ||
+        !aligned4(seqlens) || !aligned16(o) || !aligned4(lse) || !aligned16(workspace))
+        return FA_ERR_ARG;
+    const fa::PageTable pt{block_table, page_size, max_pages, num_pages};
+    const int cap = max_pages * page_size;
+    if (dtype == FA_F32) {
+        fa::FwdArgs a{q, k_pages, v_pages, o, lse, B, Hq, Hkv, Nq, cap, d, scale, causal ? 1 : 0, stream};
+        return from_hip(fa::launch_fwd_f32(a, seqlens, &pt));
+    }
+    fa::DecodeArgs a{q, k_pages, v_pages, seqlens, o, lse, B, Hq * Nq, Hkv, cap, d, scale, nullptr, nullptr,
+                     nullptr, stream};
+    a.cq = causal ? Nq : 1;
+    a.pages = pt;
+    float* ws = static_cast<float*>(workspace);
+    fa::decode_workspace_layout(a, ws);
+    return from_hip(fa::launch_decode_bf16(a));
+}
+
 }  // extern "C"

@@ -174,7 +174,8 @@ template <int D, int DS, int QR>
 __global__ __launch_bounds__(64) void decode_stream_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int* __restrict__ meta, int B, int Hq, int Hkv, int Nmax, int nht, int G, float sl2, int cq) {
+    int* __restrict__ meta, int B, int Hq, int Hkv, int Nmax, int nht, int G, float sl2, int cq,
+    PageTable pt) {
     using T = StreamTile<D, DS, QR>;
     static_assert(DS <= 5, "wait_stages covers at most five stages");
     extern __shared__ __align__(16) uint16_t smem[];
@@ -273,13 +274,26 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(
             }
         }
         const int key0 = c.j * T::BK;
-        const uint16_t* kbase = K + (size_t)(c.b * Hkv + hk) * Nmax * D;
-        const uint16_t* vbase = V + (size_t)(c.b * Hkv + hk) * Nmax * D;
+        // the stage's 32 keys are consecutive rows from row0 of kbase/vbase: of the
+        // sequence's contiguous cache, or of the one page that holds them all
+        const uint16_t* kbase;
+        const uint16_t* vbase;
+        int row0;
+        if (pt.table) {
+            const int pg = min(max(pt.table[(size_t)c.b * pt.max_pages + key0 / pt.page_size], 0), pt.num_pages - 1);
+            kbase = K + ((size_t)pg * Hkv + hk) * pt.page_size * D;
+            vbase = V + ((size_t)pg * Hkv + hk) * pt.page_size * D;
+            row0 = key0 % pt.page_size;
+        } else {
+            kbase = K + (size_t)(c.b * Hkv + hk) * Nmax * D;
+            vbase = V + (size_t)(c.b * Hkv + hk) * Nmax * D;
+            row0 = key0;
+        }
 #pragma unroll
         for (int i = 0; i < T::IPT; ++i) {
             const int slot = i * 64 + lane;
             const int row = slot / (D / 8), pos = slot % (D / 8);
-            const size_t gi = (size_t)min(key0 + row, c.len - 1) * D + ((pos ^ swz<D>(row)) << 3);
+            const size_t gi = (size_t)(row0 + min(row, c.len - 1 - key0)) * D + ((pos ^ swz<D>(row)) << 3);
             __builtin_amdgcn_global_load_lds(kbase + gi, DEC_LDS_PTR(kt + i * 64 * 8), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vbase + gi, DEC_LDS_PTR(vt + i * 64 * 8), 16, 0, 0);
         }
@@ -487,7 +501,7 @@ static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
     const int G = std::max(2, std::min(kDecodeMaxWaves, ncu * per_cu) & ~1);   // even (pairs)
     hipLaunchKernelGGL(kern, dim3(G), dim3(64), T::LDS_BYTES, (hipStream_t)a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, a.part_o, a.part_lse, a.meta, a.B,
-                       a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e, a.cq);
+                       a.Hq, a.Hkv, a.Nmax, nht, G, a.scale * kLog2e, a.cq, a.pages);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_stream_combine_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, (hipStream_t)a.stream,
                        a.part_o, a.part_lse, a.meta, a.seqlens, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nmax,

@@ -380,7 +380,8 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
-                                                      int causal, float sl2, const int* __restrict__ kv_lens) {
+                                                      int causal, float sl2, const int* __restrict__ kv_lens,
+                                                      PageTable pt) {
     constexpr int DS = D / 4;   // columns per lane
     constexpr int BK = 32;      // keys per LDS block
     __shared__ float sK[BK][D + 4];
@@ -400,8 +401,6 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     if (causal) wg_end = min(kv_end, blockIdx.x * 64 + 64 + off);
 
     const float* qrow = Q + ((size_t)(b * Hq + h) * Nq + (qi < Nq ? qi : 0)) * D + part * DS;
-    const float* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
-    const float* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
 
     float q[DS], o[DS];
 #pragma unroll
@@ -416,8 +415,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         for (int e = tid; e < BK * D; e += 256) {
             const int r = e / D, c = e % D;
             const int key = key0 + r;
-            sK[r][c] = key < kv_end ? kb[(size_t)key * D + c] : 0.f;
-            sV[r][c] = key < kv_end ? vb[(size_t)key * D + c] : 0.f;
+            size_t off_k;   // element offset of (key, c) from K (and V)
+            if (pt.table) {
+                const int pg = key < kv_end ? min(max(pt.table[(size_t)b * pt.max_pages + key / pt.page_size], 0),
+                                                  pt.num_pages - 1)
+                                            : 0;
+                off_k = (((size_t)pg * Hkv + hk) * pt.page_size + key % pt.page_size) * D + c;
+            } else {
+                off_k = ((size_t)(b * Hkv + hk) * Nk + key) * D + c;
+            }
+            sK[r][c] = key < kv_end ? K[off_k] : 0.f;
+            sV[r][c] = key < kv_end ? V[off_k] : 0.f;
         }
         __syncthreads();
         float s[BK];
@@ -502,16 +510,17 @@ hipError_t launch_fwd_bf16(const FwdArgs& a) {
 }
 
 template <int D>
-static hipError_t launch_fwd_f32_t(const FwdArgs& a, const int* kv_lens) {
+static hipError_t launch_fwd_f32_t(const FwdArgs& a, const int* kv_lens, const PageTable* pages) {
     dim3 grid((a.Nq + 63) / 64, a.Hq, a.B);
     hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, (hipStream_t)a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk,
-                       a.causal, a.scale * kLog2e, kv_lens);
+                       a.causal, a.scale * kLog2e, kv_lens,
+                       pages ? *pages : PageTable{nullptr, 0, 0, 0});
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_f32(const FwdArgs& a, const int* kv_lens) {
-    return a.d == 64 ? launch_fwd_f32_t<64>(a, kv_lens) : launch_fwd_f32_t<128>(a, kv_lens);
+hipError_t launch_fwd_f32(const FwdArgs& a, const int* kv_lens, const PageTable* pages) {
+    return a.d == 64 ? launch_fwd_f32_t<64>(a, kv_lens, pages) : launch_fwd_f32_t<128>(a, kv_lens, pages);
 }
 
 }  // namespace fa

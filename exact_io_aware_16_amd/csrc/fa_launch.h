@@ -7,6 +7,14 @@
 
 namespace fa {
 
+// A paged K/V cache: pools [num_pages][Hkv][page_size][d]; key j of sequence
+// b is row j % page_size of page table[b * max_pages + j / page_size] (entries
+// are clamped to [0, num_pages)).  page_size is a multiple of 32.
+struct PageTable {
+    const int* table;
+    int page_size, max_pages, num_pages;
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -54,10 +62,13 @@ struct DecodeArgs {
     // sequence, bottom-right aligned): Hq then counts (head, token) rows, cq
     // consecutive ones per head.  1 for plain decode and non-causal chunks.
     int cq = 1;
+    // paged cache (table == nullptr: k and v are [B][Hkv][Nmax][d]); with a
+    // table, Nmax is the capacity max_pages * page_size
+    PageTable pages{nullptr, 0, 0, 0};
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_fwd_f32(const FwdArgs& a, const int* kv_lens);
+hipError_t launch_fwd_f32(const FwdArgs& a, const int* kv_lens, const PageTable* pages = nullptr);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);

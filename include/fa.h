@@ -154,6 +154,37 @@ fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_ca
                             fa_dtype_t dtype, float scale, int causal,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace fa_decode_paged needs (as fa_decode_chunk; it
+ * does not depend on the cache).  0 for shapes fa_decode_paged would reject. */
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d);
+
+/*
+ * Chunk decode against a paged KV cache: the keys and values of all sequences
+ * live in a pool of fixed-size pages, and a block table names the page that
+ * holds each run of page_size consecutive keys of a sequence (the cache layout
+ * of vLLM's PagedAttention, which unite.ai "What is FlashAttention", section
+ * "Nguồn chính để nghiên cứu FlashAttention", names as where the method meets
+ * serving; the pages define nothing further, so the layout below is this
+ * library's).  The result is exactly fa_decode_chunk's on the contiguous cache
+ * the pages spell out.
+ *   k_pages/v_pages [num_pages][Hkv][page_size][d] (each page holds page_size
+ *   consecutive keys of every K/V head); block_table [B][max_pages] int32 on
+ *   the DEVICE: key j of sequence b is row j % page_size of page
+ *   block_table[b][j / page_size].  Entries are clamped to [0, num_pages) (an
+ *   out-of-range entry gives wrong values, never an out-of-bounds read);
+ *   entries past a sequence's last page are never read.
+ *   seqlens [B] int32 on the DEVICE, clamped to [0, max_pages * page_size].
+ *   q [B,Hq,Nq,d] (Nq = 1 is plain decode, up to 64 as fa_decode_chunk), o
+ *   [B,Hq,Nq,d] in dtype, lse [B,Hq,Nq] float32; causal as fa_decode_chunk.
+ *   page_size must be a multiple of 32 (FA_ERR_UNSUPPORTED otherwise).
+ *   workspace: at least fa_decode_paged_workspace_bytes(...) bytes.
+ */
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int* block_table, const int* seqlens, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int num_pages, int page_size,
+                            int max_pages, int d, fa_dtype_t dtype, float scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,9 +129,27 @@ def test_decode_chunk_validation(lib):
     assert lib.fa_decode_chunk_workspace_bytes(2, 32, 8, 65, 1024, 128) == 0
 
 
+def test_decode_paged_validation(lib):
+    def paged(table=P, ws=P, wsb=1 << 26, d=128, Hq=32, Hkv=8, Nq=1, pages=64, psz=64, maxp=16):
+        return lib.fa_decode_paged(P, P, P, table, P, P, P, 2, Hq, Hkv, Nq, pages, psz, maxp, d, 1, 0.088, 1,
+                                   ws, wsb, N)
+    assert paged(table=N) == 1
+    assert paged(Hq=30) == 2
+    assert paged(Nq=65) == 2
+    assert paged(pages=0) == 2
+    assert paged(maxp=0) == 2
+    assert paged(psz=48) == 4      # not a multiple of 32
+    assert paged(d=96) == 4
+    assert paged(ws=N) == 5
+    need = lib.fa_decode_paged_workspace_bytes(2, 32, 8, 1, 128)
+    assert need == lib.fa_decode_workspace_bytes(2, 32, 8, 1024, 128)
+    assert paged(wsb=need - 1) == 5
+
+
 def test_binding_names_match_header():
-    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_bwd_workspace_bytes",
-              "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes", "fa_abi_version"):
+    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged", "fa_bwd_workspace_bytes",
+              "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes", "fa_decode_paged_workspace_bytes",
+              "fa_abi_version"):
         assert callable(getattr(fa, n))
 
 
