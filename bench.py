@@ -54,7 +54,8 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
-    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode", "decode_chunk"], default=None,
+    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode", "decode_chunk", "decode_paged"],
+                    default=None,
                     help="run only this row (for profiling one kernel); prints the row as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain 256 MiB device copies (known bytes) to scale rocprofv3 "
@@ -293,6 +294,46 @@ def row_decode_chunk(args, fa, W):
             "note": "caches emptied (by reading a 1 GiB buffer) before each launch"}
 
 
+def row_decode_paged(args, fa, W):
+    """The decode workload with its cache in 64-key pages at seeded random
+    positions of a page pool, reached through a block table."""
+    import numpy as np
+    import torch
+    P = 64
+    w = W.make_config(4)
+    t = upload(w)
+    sl = torch.from_numpy(w.seqlens).to("cuda:0")
+    q = t["q"]
+    mp = w.Nk // P
+    perm = torch.from_numpy(np.random.Generator(np.random.PCG64(4)).permutation(w.B * mp).astype(np.int64)).to("cuda:0")
+
+    def paged(x):   # [B, Hkv, mp*P, d] -> pool [B*mp, Hkv, P, d], page (b, p) at perm[b*mp + p]
+        pool = torch.empty((w.B * mp, w.Hkv, P, w.d), dtype=x.dtype, device="cuda:0")
+        pool[perm] = x.view(w.B, w.Hkv, mp, P, w.d).permute(0, 2, 1, 3, 4).reshape(w.B * mp, w.Hkv, P, w.d)
+        return pool
+    kp, vp = paged(t["k"]), paged(t["v"])
+    del t
+    table = perm.view(w.B, mp).to(torch.int32).contiguous()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, 1), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(1, fa.fa_decode_paged_workspace_bytes(w.B, w.Hq, w.Hkv, 1, w.d)), dtype=torch.uint8,
+                     device="cuda:0")
+    run = fa.prepare_decode_paged(q, kp, vp, table, sl, o, lse, ws, causal=True, scale=w.scale)
+    valid = int(w.seqlens.astype(np.int64).sum())
+    nbytes = valid * w.Hkv * w.d * 2 * 2 + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
+    n = max(10, args.steps // 2)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0")
+    flush.sum()
+    torch.cuda.synchronize()
+    tc, _ = time_launches(run, n, 2, before=lambda: flush.sum())
+    sc = stats(tc)
+    gbps = nbytes / (sc["median_us"] * 1e-6) / 1e9
+    return {"workload": "gqa_decode_paged_B16_Hq32_Hkv8_N32768_d128_bf16_page64", "valid_keys": valid,
+            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
+            "cold": sc, "note": "64-key pages at seeded random pool positions; caches emptied (by reading a "
+                                "1 GiB buffer) before each launch"}
+
+
 def cpu_baseline(args, head, W):
     """The fp64 oracle on the host cores, on whole heads of the headline workload,
     until the CPU budget is spent; also checks the GPU's output on those heads."""
@@ -346,7 +387,7 @@ def main():
 
     if args.only:
         fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode,
-              "decode_chunk": row_decode_chunk}[args.only]
+              "decode_chunk": row_decode_chunk, "decode_paged": row_decode_paged}[args.only]
         print(json.dumps({args.only: fn(args, fa, W)}), flush=True)
         return
 
@@ -373,6 +414,9 @@ def main():
         torch.cuda.empty_cache()
         log("row: GQA chunk decode B16 Hq32 Hkv8 Nq8 N32768 d128 bf16")
         rows["decode_chunk"] = row_decode_chunk(args, fa, W)
+        torch.cuda.empty_cache()
+        log("row: GQA decode against a paged cache (64-key pages) B16 Hq32 Hkv8 N32768 d128 bf16")
+        rows["decode_paged"] = row_decode_paged(args, fa, W)
         torch.cuda.empty_cache()
     cpu = None
     if not args.headline_only and not args.no_cpu_baseline:
