@@ -54,7 +54,8 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
-    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "decode", "decode_chunk", "decode_paged"],
+    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "fwd_bwd_gqa", "decode", "decode_chunk",
+                                       "decode_paged"],
                     default=None,
                     help="run only this row (for profiling one kernel); prints the row as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -204,9 +205,9 @@ def row_fwd_llama(args, fa, W):
             "flops_per_launch": flops, "per_step_us": avg * 1e6}
 
 
-def row_fwd_bwd(args, fa, W):
+def row_fwd_bwd(args, fa, W, **override):
     import torch
-    w = W.make_config(5)
+    w = W.make_config(5, **override)
     t = upload(w)
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     o = torch.empty_like(q)
@@ -221,7 +222,8 @@ def row_fwd_bwd(args, fa, W):
     pairs = causal_pairs(w.Nq, w.Nk)
     ff = 4.0 * w.B * w.Hq * w.d * pairs
     fb = 10.0 * w.B * w.Hq * w.d * pairs
-    return {"workload": w.name, "fwd_tflops": ff / af / 1e12, "fwd_frac_of_peak": ff / af / PEAK_BF16,
+    name = w.name if not override else f"causal_fwd_bwd_B{w.B}_Hq{w.Hq}_Hkv{w.Hkv}_N{w.Nq}_d{w.d}_bf16"
+    return {"workload": name, "fwd_tflops": ff / af / 1e12, "fwd_frac_of_peak": ff / af / PEAK_BF16,
             "bwd_tflops": fb / ab / 1e12, "bwd_frac_of_peak": fb / ab / PEAK_BF16,
             "bwd_flop_convention": "10*B*H*d*pairs (five products, recompute included)",
             "fwd_bwd_tflops": (ff + fb) / (af + ab) / 1e12, "fwd_per_step_us": af * 1e6,
@@ -387,6 +389,7 @@ def main():
 
     if args.only:
         fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode,
+              "fwd_bwd_gqa": lambda a, f, w_: row_fwd_bwd(a, f, w_, Hq=32, Hkv=8),
               "decode_chunk": row_decode_chunk, "decode_paged": row_decode_paged}[args.only]
         print(json.dumps({args.only: fn(args, fa, W)}), flush=True)
         return
@@ -408,6 +411,9 @@ def main():
         torch.cuda.empty_cache()
         log("row: causal forward + backward B2 H16 N4096 d128 bf16")
         rows["fwd_bwd"] = row_fwd_bwd(args, fa, W)
+        torch.cuda.empty_cache()
+        log("row: GQA causal forward + backward B2 Hq32 Hkv8 N4096 d128 bf16")
+        rows["fwd_bwd_gqa"] = row_fwd_bwd(args, fa, W, Hq=32, Hkv=8)
         torch.cuda.empty_cache()
         log("row: GQA decode B16 Hq32 Hkv8 N32768 d128 bf16")
         rows["decode"] = row_decode(args, fa, W)

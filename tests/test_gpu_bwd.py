@@ -38,6 +38,24 @@ def test_config5_fwd_bwd_full():
     assert_close("dV", dv, dV, TOL_BF16)
 
 
+def test_gqa_training_shape_fwd_bwd():
+    """Grouped heads at a training shape (B2 Hq32 Hkv8 N4096 d128, causal, the
+    config-5 recipe with 4 query heads per K/V head): dK and dV of a K/V head
+    are the sums over its group, formed without atomics.  The fp64 oracle
+    checks batch 0 whole (32 query heads, 8 K/V heads)."""
+    w = W.make_config(5, Hq=32, Hkv=8)
+    announce("GQA fwd+bwd B2 Hq32 Hkv8 N4096 d128 bf16 causal (oracle on batch 0)")
+    o, lse, dq, dk, dv = run_fwd_bwd(w, True)
+    q, k, v, do = (w.values(n)[:1] for n in ("q", "k", "v", "do"))
+    O, L = oracle.ref_fwd(q, k, v, causal=True, scale=w.scale)
+    assert_close("O", o[:1], O, TOL_BF16)
+    assert_close("LSE", lse[:1], L, TOL_BF16)
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, causal=True, scale=w.scale)
+    assert_close("dQ", dq[:1], dQ, TOL_BF16)
+    assert_close("dK", dk[:1], dK, TOL_BF16)
+    assert_close("dV", dv[:1], dV, TOL_BF16)
+
+
 SHAPES = [
     # (B, Hq, Hkv, Nq, Nk, d, causal)
     (1, 1, 1, 1, 1, 64, True),
