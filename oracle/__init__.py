@@ -14,6 +14,8 @@ from .attention import (  # noqa: F401
     ref_decode,
     ref_decode_chunk,
     ref_decode_paged,
+    e4m3_value,
+    ref_fwd_fp8,
     gather_pages,
     ref_fwd,
     ref_fwd_rows,

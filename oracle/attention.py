@@ -33,6 +33,11 @@ Sources (web pages; cited by title and section):
          FlashAttention": names vLLM's PagedAttention (a KV cache kept in
          fixed-size pages reached through a per-sequence block table) as where
          the method meets serving; the pages define nothing further.
+* [FP8]  same glossary, section "Flash Attention 2 và 3": FlashAttention-3 adds
+         FP8 support.  The pages give no format or scaling; the reading here is
+         OCP FP8 E4M3 inputs with one descale factor per tensor (the value of a
+         code is its E4M3 value times the descale), and the result is exact
+         attention of those values.
 * [EX]   same glossary, section "Flash Attention Vs các kỹ Thuật Khác", and
          aiunderstanding.org "FlashAttention", section "Wawasan Teknis": the
          result is the same as standard attention, not an approximation.
@@ -257,6 +262,28 @@ def ref_decode_paged(q, k_pages, v_pages, block_table, seqlens, page_size: int, 
         vb = gather_pages(v_pages, block_table, b, n, page_size)[None]
         O[b:b + 1], LSE[b:b + 1] = ref_decode_chunk(q[b:b + 1], kb, vb, [n], causal=causal, scale=scale)
     return O, LSE
+
+
+def e4m3_value(bits) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes ([FP8]): sign bit 7, exponent bits 6..3
+    (bias 7), mantissa bits 2..0; exponent 0 is subnormal (m * 2^-9); the code
+    with every exponent and mantissa bit set is NaN; there is no infinity."""
+    b = np.asarray(bits).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(8.0 + m, (e - 10).astype(np.int64)))
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, sign * mag)
+
+
+def ref_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, causal: bool = False,
+                scale: float | None = None):
+    """Exact attention of FP8 inputs ([FP8]): the values are e4m3_value(code) *
+    descale per tensor; scale defaults to 1/sqrt(d).  Returns O, LSE (float64)."""
+    q = e4m3_value(q8) * float(descale_q)
+    k = e4m3_value(k8) * float(descale_k)
+    v = e4m3_value(v8) * float(descale_v)
+    return ref_fwd(q, k, v, causal=causal, scale=scale)
 
 
 def ref_bwd(q, k, v, do, causal: bool = False, scale: float | None = None, kv_lens=None):

@@ -267,3 +267,51 @@ def test_unmutated_paged_oracle_passes():
 @pytest.mark.parametrize("name", sorted(PAGED_MUTANTS))
 def test_paged_mutant_is_caught(name):
     assert _some_check_fails(_paged_checks(PAGED_MUTANTS[name])), f"mutant {name} passed every pin"
+
+
+# FP8: plausible slips in the E4M3 decoding and the descales
+def _decode_bias8(bits):
+    return oracle.e4m3_value(bits) * 0.5
+
+
+def _decode_subnormal_as_normal(bits):
+    b = np.asarray(bits).astype(np.int64)
+    v = oracle.e4m3_value(bits)
+    e, m = (b >> 3) & 0xF, b & 7
+    return np.where((e == 0) & (m > 0), np.where(b >> 7, -1.0, 1.0) * (1 + m / 8.0) * 2.0 ** -7, v)
+
+
+def _decode_nan_as_finite(bits):
+    b = np.asarray(bits).astype(np.int64)
+    return np.where((b & 0x7F) == 0x7F, np.where(b >> 7, -480.0, 480.0), oracle.e4m3_value(bits))
+
+
+def _fp8_with_decoder(decode):
+    def fwd8(q8, k8, v8, dq, dk, dv, causal, scale):
+        return oracle.ref_fwd(decode(q8) * dq, decode(k8) * dk, decode(v8) * dv, causal=causal, scale=scale)
+    return fwd8
+
+
+def _fp8_descale_v_dropped(q8, k8, v8, dq, dk, dv, causal, scale):
+    return oracle.ref_fwd_fp8(q8, k8, v8, dq, dk, 1.0, causal=causal, scale=scale)
+
+
+FP8_MUTANTS = {
+    "decoder_bias_8": (_decode_bias8, _fp8_with_decoder(_decode_bias8)),
+    "decoder_subnormal_as_normal": (_decode_subnormal_as_normal, _fp8_with_decoder(_decode_subnormal_as_normal)),
+    "decoder_nan_as_finite": (_decode_nan_as_finite, _fp8_with_decoder(_decode_nan_as_finite)),
+    "descale_v_dropped": (oracle.e4m3_value, _fp8_descale_v_dropped),
+}
+
+
+def _fp8_checks(decode, fwd8):
+    return [lambda: pins.check_e4m3_decoder(decode), lambda: pins.check_fp8_forward(fwd8, decode)]
+
+
+def test_unmutated_fp8_oracle_passes():
+    assert not _some_check_fails(_fp8_checks(oracle.e4m3_value, pins.fp8_oracle))
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name):
+    assert _some_check_fails(_fp8_checks(*FP8_MUTANTS[name])), f"mutant {name} passed every pin"

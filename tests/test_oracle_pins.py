@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as W
 from workloads import random_case, random_lengths
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -590,3 +591,56 @@ def test_paged_brute_force():
 
 def test_paged_invariants():
     assert check_paged_invariants(paged_oracle)
+
+
+# ---------------------------------------------------------------------------
+# FP8 forward (thienlv.com glossary, section "Flash Attention 2 và 3": FP8
+# support; the format is the OCP FP8 E4M3 definition)
+# ---------------------------------------------------------------------------
+
+def check_e4m3_decoder(decode):
+    """Values fixed by the format: 1.0 = 0x38, the largest finite 448 = 0x7E, the
+    smallest normal 2^-6 = 0x08, the smallest subnormal 2^-9 = 0x01, NaN at 0x7F
+    and 0xFF, sign in bit 7; and agreement on every code with the input
+    generator's independently written table (round trip of its encoder)."""
+    v = decode(np.arange(256))
+    ok = v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    ok &= bool(np.isnan(v[0x7F]) and np.isnan(v[0xFF])) and v[0x00] == 0.0 and np.signbit(v[0x80])
+    ok &= v[0xB8] == -1.0 and v[0x3F] == 1.875 and v[0x40] == 2.0 and v[0x07] == 7 * 2.0 ** -9
+    fin = np.r_[0:0x7F, 0x80:0xFF]
+    ok &= np.array_equal(W.f32_to_e4m3_bits(v[fin]), fin.astype(np.uint8))
+    ok &= np.array_equal(v[fin], W.e4m3_bits_to_f32(fin.astype(np.uint8)).astype(np.float64))
+    return bool(ok)
+
+
+def check_fp8_forward(fwd8, decode):
+    """Brute force on tiny inputs through the generator's decoder, and the
+    descale invariants: O is linear in the V descale, LSE does not see it;
+    moving a factor between the Q and K descales changes nothing."""
+    ok = True
+    g = np.random.Generator(np.random.PCG64(700))
+    for (B, Hq, Hkv, Nq, Nk, d, causal) in [(1, 2, 1, 4, 6, 4, True), (2, 2, 2, 3, 5, 8, False)]:
+        q8 = g.integers(0, 256, (B, Hq, Nq, d)).astype(np.uint8) & 0x77   # finite codes of magnitude < 2
+        k8 = g.integers(0, 256, (B, Hkv, Nk, d)).astype(np.uint8) & 0x77
+        v8 = g.integers(0, 256, (B, Hkv, Nk, d)).astype(np.uint8) & 0xF7
+        O, L = fwd8(q8, k8, v8, 0.5, 0.25, 2.0, causal, 0.3)
+        qv, kv, vv = (W.e4m3_bits_to_f32(x).astype(np.float64) for x in (q8, k8, v8))
+        Ob, Lb = brute_attention(qv * 0.5, kv * 0.25, vv * 2.0, causal, 0.3)
+        ok &= np.allclose(O, Ob, atol=1e-12, rtol=0) and np.allclose(L, Lb, atol=1e-12, rtol=0)
+        O2, L2 = fwd8(q8, k8, v8, 0.5, 0.25, 8.0, causal, 0.3)
+        ok &= np.allclose(O2, 4.0 * O, atol=1e-12) and np.array_equal(L2, L)
+        O3, L3 = fwd8(q8, k8, v8, 2.0, 0.0625, 2.0, causal, 0.3)
+        ok &= np.allclose(O3, O, atol=1e-12) and np.allclose(L3, L, atol=1e-12)
+    return bool(ok)
+
+
+def fp8_oracle(q8, k8, v8, dq, dk, dv, causal, scale):
+    return oracle.ref_fwd_fp8(q8, k8, v8, dq, dk, dv, causal=causal, scale=scale)
+
+
+def test_e4m3_decoder():
+    assert check_e4m3_decoder(oracle.e4m3_value)
+
+
+def test_fp8_forward():
+    assert check_fp8_forward(fp8_oracle, oracle.e4m3_value)

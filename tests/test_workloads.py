@@ -65,3 +65,20 @@ def test_values_are_normal():
     w = W.make_config(2, B=1, Hq=4, Hkv=4, Nq=2048, Nk=2048)
     x = w.values("q").astype(np.float64)
     assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+
+
+def test_fp8_quantizer():
+    """Per-tensor E4M3: power-of-two descale putting max|x| within 448, every
+    value within half an E4M3 step (relative 2^-4 in the normal range), ties
+    to the even code, saturation at 448."""
+    import workloads as W
+    x = np.random.Generator(np.random.PCG64(5)).standard_normal(20000).astype(np.float32)
+    codes, s = W.fp8_quantize(x)
+    assert math.log2(s) == int(math.log2(s)) and np.abs(x).max() / s <= 448
+    back = W.e4m3_bits_to_f32(codes).astype(np.float64) * s
+    normal = np.abs(x) / s >= 2.0 ** -6
+    assert np.all(np.abs(back - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] + 1e-12)
+    assert np.all(np.abs(back - x)[~normal] <= 2.0 ** -10 * s + 1e-12)
+    assert W.f32_to_e4m3_bits(np.array([1.0625]))[0] == 0x38     # tie between 1.0 (even) and 1.125
+    assert W.f32_to_e4m3_bits(np.array([1.1875]))[0] == 0x3A     # tie between 1.125 and 1.25 (even)
+    assert W.f32_to_e4m3_bits(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]

@@ -22,6 +22,8 @@ Workloads (sizes as stated by the five benchmark configurations):
     4  GQA decode against a KV cache    B16 Hq32 Hkv8 Nmax32768 d128, bf16,
                                         lengths ~ U{4096..32768}
     5  causal forward + backward        B2 H16 N4096 d128, bf16
+
+``to_fp8`` turns any of them into per-tensor scaled FP8 E4M3 inputs.
 """
 from __future__ import annotations
 
@@ -79,6 +81,50 @@ def normal_bf16_bits(gen: np.random.Generator, shape, chunk: int = 1 << 24) -> n
         e = min(n, s + chunk)
         out[s:e] = f32_to_bf16_bits(gen.standard_normal(size=e - s, dtype=np.float32))
     return out.reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 (OCP "E4M3FN": 1 sign, 4 exponent bits with bias 7, 3 mantissa
+# bits; no infinities; S.1111.111 is NaN; largest finite 448; subnormals
+# m * 2^-9).  Host-side encoding of float32 inputs with a per-tensor scale.
+# ---------------------------------------------------------------------------
+
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the finite non-negative codes 0x00 .. 0x7E, increasing."""
+    c = np.arange(0x7F)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value (ties to the even code), saturating at
+    +-448; NaN -> 0x7F.  Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = _e4m3_positive_values()
+    ax = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(pos, ax), 1, len(pos) - 1)
+    lo = hi - 1
+    dlo, dhi = ax - pos[lo], pos[hi] - ax
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(ax == 0, 0, code).astype(np.uint8)
+    code = code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def e4m3_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact value of each E4M3 code (NaN for the two NaN codes)."""
+    b = np.asarray(bits, dtype=np.uint8)
+    pos = np.append(_e4m3_positive_values(), np.nan)
+    v = pos[b & 0x7F]
+    return np.where(b & 0x80, -v, v).astype(np.float32)
+
+
+def fp8_quantize(x: np.ndarray):
+    """Per-tensor scaled E4M3: codes of x / s and the descale s, a power of two
+    with max|x| / s <= 448 (s = 1 for an all-zero tensor)."""
+    amax = float(np.max(np.abs(x))) if np.size(x) else 0.0
+    s = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+    return f32_to_e4m3_bits(np.asarray(x, dtype=np.float64) / s), s
 
 
 # ---------------------------------------------------------------------------
@@ -232,3 +278,10 @@ def random_case(seed: int, B, Hq, Hkv, Nq, Nk, d, dtype="bf16", with_do=False, c
 def random_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, 200, seed])))
     return g.integers(lo, hi + 1, size=B, dtype=np.int64).astype(np.int32)
+
+
+def to_fp8(w: Workload) -> dict:
+    """E4M3 versions of a workload's q, k, v: per-tensor power-of-two scales
+    chosen from each tensor's largest magnitude; returns {name: (codes,
+    descale)}.  The values the method then sees are codes * descale."""
+    return {n: fp8_quantize(w.values(n)) for n in ("q", "k", "v")}
