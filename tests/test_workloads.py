@@ -1,4 +1,6 @@
 """The seeded input generators: determinism, recipe, and bf16 rounding."""
+import math
+
 import numpy as np
 import torch
 
