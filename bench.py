@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal attn fwd/bwd TFLOP/s and % MFMA peak; decode HBM GB/s"
 PEAK_BF16 = 2.5e15          # MI355X dense bf16 matrix-core peak, FLOP/s
 PEAK_HBM = 8.0e12           # MI355X HBM3E bandwidth, bytes/s
+PEAK_FP8 = 5.0e15           # MI355X dense fp8 matrix-core peak, FLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -54,7 +55,7 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
-    ap.add_argument("--only", choices=["fwd_llama", "fwd_bwd", "fwd_bwd_gqa", "decode", "decode_chunk",
+    ap.add_argument("--only", choices=["fwd_llama", "fwd_fp8", "fwd_bwd", "fwd_bwd_gqa", "decode", "decode_chunk",
                                        "decode_paged"],
                     default=None,
                     help="run only this row (for profiling one kernel); prints the row as JSON")
@@ -203,6 +204,22 @@ def row_fwd_llama(args, fa, W):
     flops = 4.0 * w.B * w.Hq * w.d * causal_pairs(w.Nq, w.Nk)
     return {"workload": w.name, "tflops": flops / avg / 1e12, "frac_of_peak": flops / avg / PEAK_BF16,
             "flops_per_launch": flops, "per_step_us": avg * 1e6}
+
+
+def row_fwd_fp8(args, fa, W):
+    """The LLaMA-shaped causal forward with E4M3 inputs (per-tensor descales)."""
+    import torch
+    w = W.make_config(3)
+    f8 = W.to_fp8(w)
+    dev = {n: torch.from_numpy(c).to("cuda:0") for n, (c, _) in f8.items()}
+    o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda:0")
+    run = fa.prepare_fwd_fp8(dev["q"], dev["k"], dev["v"], o, lse, f8["q"][1], f8["k"][1], f8["v"][1], causal=True,
+                             scale=w.scale)
+    avg, _ = time_steps(run, max(5, args.steps // 5), max(2, args.warmup // 2))
+    flops = 4.0 * w.B * w.Hq * w.d * causal_pairs(w.Nq, w.Nk)
+    return {"workload": "llama_causal_fwd_B2_H32_N8192_d128_fp8_e4m3_kout", "tflops": flops / avg / 1e12,
+            "frac_of_fp8_peak": flops / avg / PEAK_FP8, "flops_per_launch": flops, "per_step_us": avg * 1e6}
 
 
 def row_fwd_bwd(args, fa, W, **override):
@@ -389,7 +406,7 @@ def main():
 
     if args.only:
         fn = {"fwd_llama": row_fwd_llama, "fwd_bwd": row_fwd_bwd, "decode": row_decode,
-              "fwd_bwd_gqa": lambda a, f, w_: row_fwd_bwd(a, f, w_, Hq=32, Hkv=8),
+              "fwd_bwd_gqa": lambda a, f, w_: row_fwd_bwd(a, f, w_, Hq=32, Hkv=8), "fwd_fp8": row_fwd_fp8,
               "decode_chunk": row_decode_chunk, "decode_paged": row_decode_paged}[args.only]
         print(json.dumps({args.only: fn(args, fa, W)}), flush=True)
         return
@@ -408,6 +425,9 @@ def main():
     if not args.headline_only:
         log("row: causal forward B2 H32 N8192 d128 bf16")
         rows["fwd_llama"] = row_fwd_llama(args, fa, W)
+        torch.cuda.empty_cache()
+        log("row: causal forward B2 H32 N8192 d128 fp8 (E4M3)")
+        rows["fwd_fp8"] = row_fwd_fp8(args, fa, W)
         torch.cuda.empty_cache()
         log("row: causal forward + backward B2 H16 N4096 d128 bf16")
         rows["fwd_bwd"] = row_fwd_bwd(args, fa, W)

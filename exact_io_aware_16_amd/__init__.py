@@ -62,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_chunk.restype = i
     lib.fa_decode_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp]
     lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_paged.restype = i
@@ -144,6 +146,31 @@ def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q), scale,
             int(bool(causal)), _stream(stream))
     return lambda: _check(lib.fa_fwd(*args))
+
+
+def prepare_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, scale=None, stream=None):
+    """fa_fwd_fp8's arguments checked and marshalled once.  q8, k8, v8 hold E4M3
+    codes (torch.uint8 or torch.float8_e4m3fn); o is bfloat16."""
+    _dev(q8, k8, v8, o, lse)
+    torch = _torch()
+    codes = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    if q8.dtype not in codes or k8.dtype not in codes or v8.dtype not in codes:
+        raise TypeError("q8, k8, v8 must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    B, Hq, Nq, d = q8.shape
+    _, Hkv, Nk, _ = k8.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    args = (_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, float(descale_q),
+            float(descale_k), float(descale_v), scale, int(bool(causal)), _stream(stream))
+    return lambda: _check(lib.fa_fwd_fp8(*args))
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, scale=None, stream=None):
+    """Exact attention of E4M3 inputs (value = code value * descale) into bf16 ``o``."""
+    prepare_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=causal, scale=scale,
+                    stream=stream)()
 
 
 def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
@@ -314,4 +341,13 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, causal=True, scale=N
                                 device=q.device)
     fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, causal=causal, scale=scale,
                     stream=stream)
+    return o, lse
+
+
+def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, scale=None, stream=None):
+    torch = _torch()
+    B, Hq, Nq, d = q8.shape
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=causal, scale=scale, stream=stream)
     return o, lse

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libfa.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

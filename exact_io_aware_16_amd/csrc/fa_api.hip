@@ -157,6 +157,24 @@ fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_ca
     return from_hip(fa::launch_decode_bf16(a));
 }
 
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int d, float descale_q, float descale_k, float descale_v, float scale,
+                       int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (causal && Nq > Nk) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, Nq, d) || too_big(B, Hkv, Nk, d)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK || check_scale(descale_q) != FA_OK || check_scale(descale_k) != FA_OK ||
+        check_scale(descale_v) != FA_OK)
+        return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ARG;
+    fa::Fp8Args a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, descale_q, descale_k, descale_v, scale, causal ? 1 : 0,
+                  stream};
+    return from_hip(fa::launch_fwd_fp8(a));
+}
+
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d) {
     return fa_decode_chunk_workspace_bytes(B, Hq, Hkv, Nq, 1, d);
 }

@@ -73,6 +73,20 @@ hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 
+// FP8 forward: q, k, v E4M3 codes with per-tensor descales; o bfloat16.
+struct Fp8Args {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk, d;
+    float descale_q, descale_k, descale_v, scale;
+    int causal;
+    void* stream;
+};
+hipError_t launch_fwd_fp8(const Fp8Args& a);
+
 // Workspace of the decode path: partial results for at most
 // (B * Hkv * ceil(g / 32) + kDecodeMaxWaves) slots of min(g, 32) rows each,
 // plus B + 1 stage-prefix integers.

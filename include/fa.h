@@ -154,6 +154,27 @@ fa_status_t fa_decode_chunk(const void* q, const void* k_cache, const void* v_ca
                             fa_dtype_t dtype, float scale, int causal,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 forward: exact attention of FP8 inputs (thienlv.com glossary "Flash
+ * Attention Là Gì?", section "Flash Attention 2 và 3": FlashAttention-3 adds
+ * FP8 support; format and scaling are this library's reading).
+ *   q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]: OCP FP8 E4M3 codes (one byte each; 1 sign,
+ *   4 exponent bits of bias 7, 3 mantissa bits, max 448, S.1111.111 = NaN);
+ *   the value of an element is its E4M3 value times the tensor's descale
+ *   (descale_q, descale_k, descale_v: finite, > 0).  o [B,Hq,Nq,d] bfloat16;
+ *   lse [B,Hq,Nq] float32 = ln sum_j exp(scale * q_i . k_j) of those values.
+ *   Both products run on FP8 matrix cores with float32 accumulation; the
+ *   softmax weights are rounded to E4M3 (as 2^8 P, round to nearest even)
+ *   for the second product, so O differs from exact attention by at most
+ *   2^-4 max_j |v_j| (plus the bf16 rounding of O); lse does not see that
+ *   rounding.  Other conventions as fa_fwd (causal bottom-right, GQA,
+ *   d = 64 or 128).
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       float descale_q, float descale_k, float descale_v, float scale, int causal,
+                       void* stream);
+
 /* Bytes of device workspace fa_decode_paged needs (as fa_decode_chunk; it
  * does not depend on the cache).  0 for shapes fa_decode_paged would reject. */
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d);

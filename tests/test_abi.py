@@ -146,8 +146,23 @@ def test_decode_paged_validation(lib):
     assert paged(wsb=need - 1) == 5
 
 
+def test_fwd_fp8_validation(lib):
+    def f8(q=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, dq=1.0, dk=1.0, dv=1.0, scale=0.088, causal=0):
+        return lib.fa_fwd_fp8(q, P, P, P, P, B, Hq, Hkv, Nq, Nk, d, dq, dk, dv, scale, causal, N)
+    assert f8(q=N) == 1
+    assert f8(B=0) == 2
+    assert f8(Hq=3, Hkv=2) == 2
+    assert f8(causal=1, Nq=9, Nk=8) == 2
+    assert f8(d=96) == 4
+    assert f8(dq=0.0) == 7
+    assert f8(dv=float("nan")) == 7
+    assert f8(dk=-1.0) == 7
+    assert f8(q=ctypes.c_void_p(0x1008)) == 7
+
+
 def test_binding_names_match_header():
-    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged", "fa_bwd_workspace_bytes",
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged",
+              "fa_bwd_workspace_bytes",
               "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes", "fa_decode_paged_workspace_bytes",
               "fa_abi_version"):
         assert callable(getattr(fa, n))
