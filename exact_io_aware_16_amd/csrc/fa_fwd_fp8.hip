@@ -27,11 +27,17 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
-#ifndef FP8_NW
-#define FP8_NW 4         // waves per workgroup
+#ifndef FP8_NW128
+#define FP8_NW128 4      // waves per workgroup, d = 128
 #endif
-#ifndef FP8_S
-#define FP8_S 3          // ring stages
+#ifndef FP8_S128
+#define FP8_S128 3       // ring stages, d = 128
+#endif
+#ifndef FP8_NW64
+#define FP8_NW64 4       // waves per workgroup, d = 64
+#endif
+#ifndef FP8_S64
+#define FP8_S64 3        // ring stages, d = 64
 #endif
 
 namespace fa {
@@ -264,16 +270,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int NW, int S, bool CAUSAL>
 hipError_t launch_fp8_t(const Fp8Args& a) {
-    using T = Fp8Tile<D, FP8_NW, FP8_S>;
+    using T = Fp8Tile<D, NW, S>;
     const int nqb = (a.Nq + T::BM - 1) / T::BM;
     const int BH = a.B * a.Hq;
-    auto kern = fwd_fp8_kernel<D, FP8_NW, FP8_S, CAUSAL>;
+    auto kern = fwd_fp8_kernel<D, NW, S, CAUSAL>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(FP8_NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
+    hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
                        (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq,
                        a.Hkv, a.Nq, a.Nk, nqb, BH, a.scale * a.descale_q * a.descale_k * kLog2e, a.descale_v);
     return hipGetLastError();
@@ -282,8 +288,10 @@ hipError_t launch_fp8_t(const Fp8Args& a) {
 }  // namespace
 
 hipError_t launch_fwd_fp8(const Fp8Args& a) {
-    if (a.d == 64) return a.causal ? launch_fp8_t<64, true>(a) : launch_fp8_t<64, false>(a);
-    return a.causal ? launch_fp8_t<128, true>(a) : launch_fp8_t<128, false>(a);
+    if (a.d == 64)
+        return a.causal ? launch_fp8_t<64, FP8_NW64, FP8_S64, true>(a) : launch_fp8_t<64, FP8_NW64, FP8_S64, false>(a);
+    return a.causal ? launch_fp8_t<128, FP8_NW128, FP8_S128, true>(a)
+                    : launch_fp8_t<128, FP8_NW128, FP8_S128, false>(a);
 }
 
 }  // namespace fa
