@@ -25,10 +25,11 @@ def lib():
     return fa.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
-              "fa_abi_version", "fa_status_str"):
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged",
+              "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes",
+              "fa_decode_paged_workspace_bytes", "fa_abi_version", "fa_status_str"):
         assert n in names, names
 
 
