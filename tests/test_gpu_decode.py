@@ -133,3 +133,55 @@ def test_decode_workspace_needs_no_initialisation_and_is_reusable():
     q2, k2, v2 = q[:2, :4], k[:2, :1], v[:2, :1]
     check([2500, 900], qx=qd[:2, :4].contiguous(), kx=kd[:2, :1].contiguous(), vx=vd[:2, :1].contiguous(),
           ref=(q2, k2, v2))
+
+
+def _hash_vals(j, c, salt, xp):
+    """Cache entries as an integer hash of (key j, column c): multiples of 1/64
+    in [-2, 2), exact in bfloat16, computed identically by numpy and torch."""
+    h = (j * 2654435761 + c * 40503 + salt * 97) & 0xFFFFFFFF
+    return (((h >> 13) & 0xFF) - 128).astype(xp.float32) / 64.0 if xp is np else \
+        (((h >> 13) & 0xFF) - 128).to(xp.float32) / 64.0
+
+
+def test_decode_cache_beyond_2gib():
+    """One sequence of 12.5M cached keys at d = 128 (3.2 GB each for K and V):
+    element offsets stay below 2^31 but byte offsets pass 2^31 and 2^32.  The
+    cache is built on the GPU from an integer hash and re-derived on the host,
+    chunk by chunk, for the fp64 oracle of the 4 query heads."""
+    import torch
+    N, d, Hq, chunk = 12_500_000, 128, 4, 1 << 20
+    announce(f"decode over a {N}-key cache (K and V {N * d * 2 / 2**30:.1f} GiB each)")
+    dev = "cuda:0"
+    k = torch.empty((1, 1, N, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    cols = torch.arange(d, device=dev, dtype=torch.int64)[None, :]
+    for j0 in range(0, N, chunk):
+        j = torch.arange(j0, min(N, j0 + chunk), device=dev, dtype=torch.int64)[:, None]
+        k[0, 0, j0:j0 + j.shape[0]] = _hash_vals(j, cols, 1, torch).to(torch.bfloat16)
+        v[0, 0, j0:j0 + j.shape[0]] = _hash_vals(j, cols, 2, torch).to(torch.bfloat16)
+    q32 = np.random.Generator(np.random.PCG64(13)).standard_normal((1, Hq, 1, d)).astype(np.float32)
+    q_bits = W.f32_to_bf16_bits(q32)
+    qv = W.bf16_bits_to_f32(q_bits).astype(np.float64)[0, :, 0]          # [Hq, d]
+    o, lse = fa.decode(to_device(q_bits), k, v, to_device(np.array([N], dtype=np.int32)))
+    o, lse = to_host(o)[0, :, 0], to_host(lse)[0]
+    del k, v
+    torch.cuda.empty_cache()
+    # oracle: exact softmax over all N keys, streamed in chunks with a running max
+    scale = 1.0 / np.sqrt(d)
+    m = np.full(Hq, -np.inf); l = np.zeros(Hq); acc = np.zeros((Hq, d))
+    colsn = np.arange(d, dtype=np.int64)[None, :]
+    for j0 in range(0, N, chunk):
+        j = np.arange(j0, min(N, j0 + chunk), dtype=np.int64)[:, None]
+        kc = _hash_vals(j, colsn, 1, np).astype(np.float64)
+        vc = _hash_vals(j, colsn, 2, np).astype(np.float64)
+        s = scale * (qv @ kc.T)                     # [Hq, chunk]
+        mn = np.maximum(m, s.max(axis=1))
+        c = np.exp(m - mn)
+        e = np.exp(s - mn[:, None])
+        l = l * c + e.sum(axis=1)
+        acc = acc * c[:, None] + e @ vc
+        m = mn
+    O = acc / l[:, None]
+    L = m + np.log(l)
+    assert_close("O", o, O, TOL_BF16)
+    assert_close("LSE", lse, L, TOL_BF16)
