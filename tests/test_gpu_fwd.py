@@ -128,3 +128,47 @@ def test_invalid_arguments_raise():
     q = torch.zeros(1, 2, 8, 96, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(RuntimeError, match="FA_ERR_UNSUPPORTED"):
         fa.fwd(q, q, q)
+
+
+def test_forward_q_and_o_beyond_2gib():
+    """MQA with 64 query heads of 200000 rows and 64 keys, d = 128, non-causal:
+    Q and O are 3.3 GB each (byte offsets past 2^31), the work small.  Q, K and
+    V are an integer hash of their indices (multiples of 1/64 in [-2, 2), exact
+    in bfloat16), built on the GPU and re-derived on the host for the sampled
+    rows (the last rows of the last head among them)."""
+    import torch
+    Hq, Nq, Nk, d = 64, 200_000, 64, 128
+
+    def hv(i, c, salt, xp):
+        h = (i * 2654435761 + c * 40503 + salt * 97) & 0xFFFFFFFF
+        x = ((h >> 13) & 0xFF) - 128
+        return x.astype(np.float64) / 64.0 if xp is np else x.to(torch.float32) / 64.0
+    announce(f"forward with Q and O of {Hq * Nq * d * 2 / 2**30:.1f} GiB each")
+    dev = "cuda:0"
+    q = torch.empty((1, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+    cols = torch.arange(d, device=dev, dtype=torch.int64)[None, :]
+    rows_per_head = torch.arange(Nq, device=dev, dtype=torch.int64)[:, None]
+    for h in range(Hq):
+        q[0, h] = hv(rows_per_head + h * Nq, cols, 3, torch).to(torch.bfloat16)
+    kj = torch.arange(Nk, device=dev, dtype=torch.int64)[:, None]
+    k = hv(kj, cols, 1, torch).to(torch.bfloat16)[None, None].contiguous()
+    v = hv(kj, cols, 2, torch).to(torch.bfloat16)[None, None].contiguous()
+    o, lse = fa.fwd(q, k, v, causal=False)
+    rng = np.random.Generator(np.random.PCG64(17))
+    heads = np.r_[rng.integers(0, Hq, 500), [Hq - 1] * 12]
+    rws = np.r_[rng.integers(0, Nq, 500), np.arange(Nq - 12, Nq)]
+    og = o[0, torch.from_numpy(heads).to(dev), torch.from_numpy(rws).to(dev)].float().cpu().numpy().astype(np.float64)
+    lg = lse[0, torch.from_numpy(heads).to(dev), torch.from_numpy(rws).to(dev)].cpu().numpy().astype(np.float64)
+    del q, o
+    torch.cuda.empty_cache()
+    colsn = np.arange(d, dtype=np.int64)[None, :]
+    kn = hv(np.arange(Nk, dtype=np.int64)[:, None], colsn, 1, np)
+    vn = hv(np.arange(Nk, dtype=np.int64)[:, None], colsn, 2, np)
+    qn = hv((rws + heads * Nq).astype(np.int64)[:, None], colsn, 3, np)
+    s = (qn @ kn.T) / np.sqrt(d)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    O = (e / e.sum(axis=1, keepdims=True)) @ vn
+    L = m[:, 0] + np.log(e.sum(axis=1))
+    assert_close("O[rows]", og, O, TOL_BF16)
+    assert_close("LSE[rows]", lg, L, TOL_BF16)
