@@ -1,5 +1,7 @@
 """fa_decode on the GPU against the fp64 oracle: the full GQA decode
 configuration, ragged cache lengths, group sizes, and a poisoned cache tail."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -135,19 +137,12 @@ def test_decode_workspace_needs_no_initialisation_and_is_reusable():
           ref=(q2, k2, v2))
 
 
-def _hash_vals(j, c, salt, xp):
-    """Cache entries as an integer hash of (key j, column c): multiples of 1/64
-    in [-2, 2), exact in bfloat16, computed identically by numpy and torch."""
-    h = (j * 2654435761 + c * 40503 + salt * 97) & 0xFFFFFFFF
-    return (((h >> 13) & 0xFF) - 128).astype(xp.float32) / 64.0 if xp is np else \
-        (((h >> 13) & 0xFF) - 128).to(xp.float32) / 64.0
-
-
 def test_decode_cache_beyond_2gib():
     """One sequence of 12.5M cached keys at d = 128 (3.2 GB each for K and V):
-    element offsets stay below 2^31 but byte offsets pass 2^31 and 2^32.  The
-    cache is built on the GPU from an integer hash and re-derived on the host,
-    chunk by chunk, for the fp64 oracle of the 4 query heads."""
+    element offsets stay below 2^31 but byte offsets pass 2^31 (a signed
+    32-bit byte offset would wrap).  The cache is built on the GPU from an
+    integer hash of (key, column) and re-derived on the host, chunk by chunk,
+    for the fp64 oracle of the 4 query heads."""
     import torch
     N, d, Hq, chunk = 12_500_000, 128, 4, 1 << 20
     announce(f"decode over a {N}-key cache (K and V {N * d * 2 / 2**30:.1f} GiB each)")
@@ -157,8 +152,8 @@ def test_decode_cache_beyond_2gib():
     cols = torch.arange(d, device=dev, dtype=torch.int64)[None, :]
     for j0 in range(0, N, chunk):
         j = torch.arange(j0, min(N, j0 + chunk), device=dev, dtype=torch.int64)[:, None]
-        k[0, 0, j0:j0 + j.shape[0]] = _hash_vals(j, cols, 1, torch).to(torch.bfloat16)
-        v[0, 0, j0:j0 + j.shape[0]] = _hash_vals(j, cols, 2, torch).to(torch.bfloat16)
+        k[0, 0, j0:j0 + j.shape[0]] = W.hash_values(j, cols, 1).to(torch.bfloat16)
+        v[0, 0, j0:j0 + j.shape[0]] = W.hash_values(j, cols, 2).to(torch.bfloat16)
     q32 = np.random.Generator(np.random.PCG64(13)).standard_normal((1, Hq, 1, d)).astype(np.float32)
     q_bits = W.f32_to_bf16_bits(q32)
     qv = W.bf16_bits_to_f32(q_bits).astype(np.float64)[0, :, 0]          # [Hq, d]
@@ -170,10 +165,13 @@ def test_decode_cache_beyond_2gib():
     scale = 1.0 / np.sqrt(d)
     m = np.full(Hq, -np.inf); l = np.zeros(Hq); acc = np.zeros((Hq, d))
     colsn = np.arange(d, dtype=np.int64)[None, :]
+    pool = ThreadPoolExecutor(8)
+
+    def gen(j, salt):   # the hash of one chunk of keys, its rows split over threads
+        return np.concatenate(list(pool.map(lambda b: W.hash_values(b, colsn, salt), np.array_split(j, 8))))
     for j0 in range(0, N, chunk):
         j = np.arange(j0, min(N, j0 + chunk), dtype=np.int64)[:, None]
-        kc = _hash_vals(j, colsn, 1, np).astype(np.float64)
-        vc = _hash_vals(j, colsn, 2, np).astype(np.float64)
+        kc, vc = gen(j, 1), gen(j, 2)
         s = scale * (qv @ kc.T)                     # [Hq, chunk]
         mn = np.maximum(m, s.max(axis=1))
         c = np.exp(m - mn)
@@ -181,6 +179,7 @@ def test_decode_cache_beyond_2gib():
         l = l * c + e.sum(axis=1)
         acc = acc * c[:, None] + e @ vc
         m = mn
+    pool.shutdown()
     O = acc / l[:, None]
     L = m + np.log(l)
     assert_close("O", o, O, TOL_BF16)

@@ -133,26 +133,21 @@ def test_invalid_arguments_raise():
 def test_forward_q_and_o_beyond_2gib():
     """MQA with 64 query heads of 200000 rows and 64 keys, d = 128, non-causal:
     Q and O are 3.3 GB each (byte offsets past 2^31), the work small.  Q, K and
-    V are an integer hash of their indices (multiples of 1/64 in [-2, 2), exact
-    in bfloat16), built on the GPU and re-derived on the host for the sampled
-    rows (the last rows of the last head among them)."""
+    V come from an integer hash of their indices, built on the GPU and
+    re-derived on the host for the sampled rows (the last rows of the last head
+    among them)."""
     import torch
     Hq, Nq, Nk, d = 64, 200_000, 64, 128
-
-    def hv(i, c, salt, xp):
-        h = (i * 2654435761 + c * 40503 + salt * 97) & 0xFFFFFFFF
-        x = ((h >> 13) & 0xFF) - 128
-        return x.astype(np.float64) / 64.0 if xp is np else x.to(torch.float32) / 64.0
     announce(f"forward with Q and O of {Hq * Nq * d * 2 / 2**30:.1f} GiB each")
     dev = "cuda:0"
     q = torch.empty((1, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
     cols = torch.arange(d, device=dev, dtype=torch.int64)[None, :]
     rows_per_head = torch.arange(Nq, device=dev, dtype=torch.int64)[:, None]
     for h in range(Hq):
-        q[0, h] = hv(rows_per_head + h * Nq, cols, 3, torch).to(torch.bfloat16)
+        q[0, h] = W.hash_values(rows_per_head + h * Nq, cols, 3).to(torch.bfloat16)
     kj = torch.arange(Nk, device=dev, dtype=torch.int64)[:, None]
-    k = hv(kj, cols, 1, torch).to(torch.bfloat16)[None, None].contiguous()
-    v = hv(kj, cols, 2, torch).to(torch.bfloat16)[None, None].contiguous()
+    k = W.hash_values(kj, cols, 1).to(torch.bfloat16)[None, None].contiguous()
+    v = W.hash_values(kj, cols, 2).to(torch.bfloat16)[None, None].contiguous()
     o, lse = fa.fwd(q, k, v, causal=False)
     rng = np.random.Generator(np.random.PCG64(17))
     heads = np.r_[rng.integers(0, Hq, 500), [Hq - 1] * 12]
@@ -162,9 +157,9 @@ def test_forward_q_and_o_beyond_2gib():
     del q, o
     torch.cuda.empty_cache()
     colsn = np.arange(d, dtype=np.int64)[None, :]
-    kn = hv(np.arange(Nk, dtype=np.int64)[:, None], colsn, 1, np)
-    vn = hv(np.arange(Nk, dtype=np.int64)[:, None], colsn, 2, np)
-    qn = hv((rws + heads * Nq).astype(np.int64)[:, None], colsn, 3, np)
+    kn = W.hash_values(np.arange(Nk, dtype=np.int64)[:, None], colsn, 1)
+    vn = W.hash_values(np.arange(Nk, dtype=np.int64)[:, None], colsn, 2)
+    qn = W.hash_values((rws + heads * Nq).astype(np.int64)[:, None], colsn, 3)
     s = (qn @ kn.T) / np.sqrt(d)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)

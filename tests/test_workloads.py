@@ -84,3 +84,20 @@ def test_fp8_quantizer():
     assert W.f32_to_e4m3_bits(np.array([1.0625]))[0] == 0x38     # tie between 1.0 (even) and 1.125
     assert W.f32_to_e4m3_bits(np.array([1.1875]))[0] == 0x3A     # tie between 1.125 and 1.25 (even)
     assert W.f32_to_e4m3_bits(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]
+
+
+def test_hash_values():
+    """The index hash gives the same values from numpy and torch, on the 1/64
+    grid in [-2, 2), with mean ~0, variance ~ that of U[-2, 2) and rows that are
+    nearly uncorrelated (a linear hash fails the last check)."""
+    import torch
+    rows = np.arange(4096, dtype=np.int64)[:, None] + 12_000_000
+    cols = np.arange(128, dtype=np.int64)[None, :]
+    a = W.hash_values(rows, cols, 3)
+    b = W.hash_values(torch.from_numpy(rows), torch.from_numpy(cols), 3).numpy()
+    assert np.array_equal(a, b.astype(np.float64))
+    assert np.array_equal(a * 64, np.round(a * 64)) and a.min() >= -2 and a.max() < 2
+    assert abs(a.mean()) < 0.02 and abs(a.var() - 4 / 3) < 0.03
+    c = np.corrcoef(a)[np.triu_indices(a.shape[0], 1)]
+    assert np.abs(c).max() < 0.45 and np.abs(c).mean() < 0.1
+    assert not np.array_equal(a, W.hash_values(rows, cols, 4))

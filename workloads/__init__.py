@@ -24,6 +24,10 @@ Workloads (sizes as stated by the five benchmark configurations):
     5  causal forward + backward        B2 H16 N4096 d128, bf16
 
 ``to_fp8`` turns any of them into per-tensor scaled FP8 E4M3 inputs.
+
+``hash_values`` builds inputs too large to draw and copy from the host: an
+integer hash of each element's (row, column) index, evaluated on the device
+and re-evaluated on the host for any row the oracle needs.
 """
 from __future__ import annotations
 
@@ -285,3 +289,40 @@ def to_fp8(w: Workload) -> dict:
     chosen from each tensor's largest magnitude; returns {name: (codes,
     descale)}.  The values the method then sees are codes * descale."""
     return {n: fp8_quantize(w.values(n)) for n in ("q", "k", "v")}
+
+
+_M32 = 0xFFFFFFFF
+_HASH_VALUE = (np.arange(256) - 128) / 64.0
+
+
+def hash_values(row, col, salt: int):
+    """Values in [-2, 2) on the 1/64 grid (exact in bfloat16) from a 32-bit
+    hash of (row, column, salt).  The key is a linear mix of the three; the
+    murmur3 32-bit finaliser (xor-shift 16, multiply 0x85EBCA6B, xor-shift 13,
+    multiply 0xC2B2AE35, xor-shift 16) then spreads it, so rows and columns
+    come out as good as independent (a linear key alone leaves the rows nearly
+    parallel).  ``row`` and ``col`` are int64 numpy arrays or torch tensors on
+    any device (broadcast together); torch works in int64 masked to 32 bits,
+    numpy in uint32, and both give the same values.
+    Returns float64 for numpy, float32 for torch."""
+    if isinstance(row, np.ndarray):
+        # uint32 arithmetic wraps modulo 2^32 by itself; the key's row and
+        # column parts are formed on the small operands before broadcasting
+        u = np.uint32
+        with np.errstate(over="ignore"):
+            hr = (np.asarray(row) & _M32).astype(u) * u(0x9E3779B1) + u((salt * 0x68E31DA4) & _M32)
+            h = hr + (np.asarray(col) & _M32).astype(u) * u(0x7FEB352D)
+            h ^= h >> u(16)
+            h *= u(0x85EBCA6B)
+            h ^= h >> u(13)
+            h *= u(0xC2B2AE35)
+            h ^= h >> u(16)
+        return _HASH_VALUE[(h >> u(8)) & u(0xFF)]
+    import torch
+    h = (row * 0x9E3779B1 + col * 0x7FEB352D + salt * 0x68E31DA4) & _M32
+    h = h ^ (h >> 16)
+    h = (h * 0x85EBCA6B) & _M32
+    h = h ^ (h >> 13)
+    h = (h * 0xC2B2AE35) & _M32
+    h = h ^ (h >> 16)
+    return (((h >> 8) & 0xFF) - 128).to(torch.float32) / 64.0
