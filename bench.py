@@ -16,7 +16,11 @@ Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  Times come from HIP events recorded on the stream the kernels are
 launched on (torch's current stream): a step is one call of the library, K
 steps run back to back between one pair of events (arguments marshalled once,
-so the host keeps the GPU fed), synchronised on both sides.  The headline also
+so the host keeps the GPU fed), synchronised on both sides.  Each timed
+section first runs its own step untimed for ``--settle`` seconds (default 0.3)
+and then W warmup steps: the GPU raises its clock over the first tens of
+milliseconds of sustained load, and timing inside that ramp (after host-side
+set-up left the GPU idle) under-reports a 45 us kernel by up to 20%.  The headline also
 reports the same launches timed one at a time ("isolated_launch"), where the
 GPU idles between launches.  Decode's cache-cold figures need a cache-emptying
 pass before every launch, so they are timed one launch at a time.
@@ -55,6 +59,8 @@ def parse_args():
     ap.add_argument("--headline-only", action="store_true", help="skip the other rows and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU budget of the oracle sample")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed load before each timed section, so the GPU clock has ramped up")
     ap.add_argument("--only", choices=["fwd_llama", "fwd_fp8", "fwd_bwd", "fwd_bwd_gqa", "decode", "decode_chunk",
                                        "decode_paged"],
                     default=None,
@@ -73,11 +79,33 @@ def log(msg):
 # timing helpers (HIP events on the launch stream)
 # ---------------------------------------------------------------------------
 
+SETTLE_S = 0.3   # seconds of untimed load before each timed section (--settle)
+
+
+def settle(fn, before=None):
+    """Run the step untimed, in batches of 16 with a synchronisation after each,
+    for SETTLE_S seconds of wall time.  The GPU raises its clock over the first
+    tens of milliseconds of sustained load (a d=64 forward runs 54 us per
+    launch at first and 45 us after ~60 ms), and every section below is timed
+    after host-side set-up during which the GPU idled, so without this the first
+    few milliseconds of each section measure the ramp rather than the kernel."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(16):
+            if before:
+                before()
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_steps(fn, steps, warmup):
     """K back-to-back steps between one pair of HIP events on the launch stream
-    (torch's current stream), synchronised on both sides; returns seconds per
-    step and the host wall time of the timed region."""
+    (torch's current stream), synchronised on both sides, after the clock
+    settle and W warmup steps; returns seconds per step and the host wall time
+    of the timed region."""
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -93,8 +121,10 @@ def time_steps(fn, steps, warmup):
 
 
 def time_launches(fn, steps, warmup, before=None):
-    """Per-launch event pairs; returns (list of seconds, total seconds of the timed region)."""
+    """Per-launch event pairs (after the clock settle and W warmup launches);
+    returns (list of seconds, total seconds of the timed region)."""
     import torch
+    settle(fn, before)
     for _ in range(warmup):
         if before:
             before()
@@ -388,7 +418,9 @@ def cpu_baseline(args, head, W):
 
 
 def main():
+    global SETTLE_S
     args = parse_args()
+    SETTLE_S = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the multi-GPU path is not built. "
               "Run with --gpus 1.", file=sys.stderr)
@@ -467,6 +499,7 @@ def main():
                    "flops_per_step": head["flops"], "flop_convention": "4*B*H*d*N(N+1)/2"},
         "frac_of_peak": head["flops"] / head["avg_s"] / PEAK_BF16,
         "timing": head["stats"],
+        "clock_settle_s": SETTLE_S,
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "rows": rows,
