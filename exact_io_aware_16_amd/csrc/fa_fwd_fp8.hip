@@ -27,6 +27,10 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// output rows staged through LDS and written whole with streaming stores (as the bf16 forward)
+#ifndef FP8_LDS_EPI
+#define FP8_LDS_EPI 1
+#endif
 #ifndef FP8_NW128
 #define FP8_NW128 4      // waves per workgroup, d = 128
 #endif
@@ -253,6 +257,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
     const int qi = qw + n;
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? descale_v / l_tot : 0.f;
+    if constexpr (FP8_LDS_EPI) {
+        // O rows staged through this wave's part of the idle ring and written
+        // whole with streaming stores (16 bytes per lane, complete rows per
+        // instruction), as in the bf16 forward
+        static_assert(NW * 32 * D * 2 <= T::LDS_BYTES, "output tiles must fit in the ring");
+        constexpr int OCPR = D / 8;      // 16-byte chunks per bf16 row
+        constexpr int RPI = 64 / OCPR;   // rows per store instruction
+        __syncthreads();                 // every wave is past its last ring read
+        uint16_t* so = reinterpret_cast<uint16_t*>(smem8) + wave * 32 * D;
+#pragma unroll
+        for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = md * 4 + g;
+                const uint32_t lo = pack_bf16x2(ot[md][g * 4 + 0] * inv, ot[md][g * 4 + 1] * inv);
+                const uint32_t hi = pack_bf16x2(ot[md][g * 4 + 2] * inv, ot[md][g * 4 + 3] * inv);
+                *reinterpret_cast<u32x2*>(so + n * D + ((c ^ (n & (OCPR - 1))) << 3) + hf * 4) = u32x2{lo, hi};
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int r = k * RPI + lane / OCPR, c = lane % OCPR;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * D + ((c ^ (r & (OCPR - 1))) << 3));
+            if (qw + r < Nq)
+                __builtin_nontemporal_store(
+                    val, reinterpret_cast<u32x4*>(O + ((size_t)(b * Hq + h) * Nq + qw + r) * D + c * 8));
+        }
+        if (qi < Nq && hf == 0)
+            __builtin_nontemporal_store(l_tot > 0.f ? (m_run + log2_fast(l_tot) - kPScaleLog2) * kLn2 : kNegInf,
+                                        LSE + (size_t)(b * Hq + h) * Nq + qi);
+        return;
+    }
     if (qi < Nq) {
         uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
 #pragma unroll
