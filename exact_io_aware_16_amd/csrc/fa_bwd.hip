@@ -29,6 +29,12 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// gradient tiles staged through LDS and written as whole 128-byte row segments
+// with streaming stores (1), or stored from the accumulator layout (0)
+#ifndef BWD_LDS_EPI
+#define BWD_LDS_EPI 1
+#endif
+
 namespace fa {
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -40,6 +46,52 @@ __device__ __forceinline__ void store_grad4(float* dst, float a, float b, float 
 }
 __device__ __forceinline__ void store_grad4(uint16_t* dst, float a, float b, float c, float d) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// Store one wave's 32 x D gradient tile, held in the 32x32 MFMA accumulator
+// layout (lane (n, hf): row n, columns md*32 + 8(i/4) + 4hf + i%4 of acc[md][i]),
+// times `mul`, as whole 128-byte row segments.  Stored directly each
+// instruction would write 16 (fp32) or 8 (bf16) bytes of 32 rows, partial
+// lines that wait dirty in L2 for the write-back at kernel end.  Here each
+// 128-byte column band of the tile is staged in the wave's 4 KB of LDS (row r,
+// 16-byte chunk c at chunk c ^ (r mod 8)), read back by rows and written 16
+// bytes per lane, 8 complete segments per instruction, with streaming stores.
+// Rows r >= nrows are not written.  The wave's LDS operations complete in
+// order, so a band's writes never overtake the previous band's reads.
+template <int D, typename G>
+__device__ __forceinline__ void store_tile_rows(G* base, int nrows, const f32x16* acc, float mul, uint8_t* stage,
+                                                int lane) {
+    constexpr int PW = 128 / (int)sizeof(G);   // columns per band
+    const int n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < D / PW; ++p) {
+#pragma unroll
+        for (int mdl = 0; mdl < PW / 32; ++mdl) {
+            const int md = p * (PW / 32) + mdl;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float a0 = acc[md][g * 4] * mul, a1 = acc[md][g * 4 + 1] * mul;
+                const float a2 = acc[md][g * 4 + 2] * mul, a3 = acc[md][g * 4 + 3] * mul;
+                if constexpr (sizeof(G) == 4) {
+                    const int c = 2 * g + hf;
+                    *reinterpret_cast<f32x4*>(stage + n * 128 + ((c ^ (n & 7)) << 4)) = f32x4{a0, a1, a2, a3};
+                } else {
+                    const int c = mdl * 4 + g;
+                    *reinterpret_cast<u32x2*>(stage + n * 128 + ((c ^ (n & 7)) << 4) + hf * 8) =
+                        u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the band is in LDS
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = k * 8 + (lane >> 3), c = lane & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 128 + ((c ^ (r & 7)) << 4));
+            if (r < nrows)
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base + (size_t)r * D) + p * 128 + c * 16));
+        }
+    }
 }
 
 }  // namespace
@@ -223,6 +275,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
+    if constexpr (BWD_LDS_EPI) {
+        static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
+        __syncthreads();   // every wave is past its last ring read: the ring stages the output
+        store_tile_rows<D>(dQ + ((size_t)(b * Hq + h) * Nq + qw) * D, Nq - qw, acc, scale,
+                           reinterpret_cast<uint8_t*>(smem) + wave * 4096, lane);
+        return;
+    }
     if (qi < Nq) {
         G* out = dQ + ((size_t)(b * Hq + h) * Nq + qi) * D;
 #pragma unroll
@@ -563,6 +622,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
+    if constexpr (BWD_LDS_EPI) {
+        static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
+        __syncthreads();   // every wave is past its last ring read: the ring stages the output
+        const size_t o = ((size_t)(b * Hkv + hk) * Nk + kw) * D;
+        uint8_t* stage = reinterpret_cast<uint8_t*>(smem) + wave * 4096;
+        store_tile_rows<D>(dK + o, Nk - kw, dk, scale, stage, lane);
+        store_tile_rows<D>(dV + o, Nk - kw, dv, 1.f, stage, lane);
+        return;
+    }
     if (kj < Nk) {
         const size_t o = ((size_t)(b * Hkv + hk) * Nk + kj) * D;
 #pragma unroll
