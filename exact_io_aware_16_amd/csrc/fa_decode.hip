@@ -127,8 +127,18 @@ __device__ __forceinline__ void wait_stages(int r) {
 // (2p, 2p+1), which the dispatcher places on an even and an odd XCD (one-wave
 // workgroup w runs on XCD w mod 8); pair p covers [p S / (G/2), (p+1) S / (G/2))
 // and its even wave the first DEC_EVEN64/64 of that.  G is even.
+// (The same integer arithmetic in 32 bits whenever S * (G/2) < 2^31, the usual
+// case: 64-bit divisions are emulated and cost the combine kernel, which
+// evaluates these per piece, far more.)
 __device__ __forceinline__ long long dec_range_start(int w, long long S, int G) {
     const int gp = G >> 1, p = w >> 1;
+    if (S * gp < (1LL << 31)) {
+        // p <= gp, so (p + 1) * S < 2^31 + S fits in 32 unsigned bits
+        const uint32_t s = (uint32_t)S, a = (uint32_t)p * s / (uint32_t)gp;
+        if ((w & 1) == 0) return a;
+        const uint32_t e = (uint32_t)(p + 1) * s / (uint32_t)gp;
+        return a + (e - a) * DEC_EVEN64 / 64;
+    }
     const long long a = (long long)p * S / gp;
     if ((w & 1) == 0) return a;
     const long long e = (long long)(p + 1) * S / gp;
@@ -137,7 +147,8 @@ __device__ __forceinline__ long long dec_range_start(int w, long long S, int G) 
 // the wave whose range holds stage st (0 <= st < S)
 __device__ __forceinline__ int dec_wave_of(long long st, long long S, int G) {
     const int gp = G >> 1;
-    const int p = (int)(((st + 1) * gp - 1) / S);
+    const int p = S * gp < (1LL << 31) ? (int)(((uint32_t)st + 1) * (uint32_t)gp - 1) / (int)S
+                                        : (int)(((st + 1) * gp - 1) / S);
     return 2 * p + (st >= dec_range_start(2 * p + 1, S, G) ? 1 : 0);
 }
 
