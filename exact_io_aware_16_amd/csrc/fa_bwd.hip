@@ -29,6 +29,11 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// D = rowsum(dO * O) and lse2 computed by the dQ kernel (1) instead of a
+// separate pass over O and dO before it (0)
+#ifndef BWD_FUSE_DELTA
+#define BWD_FUSE_DELTA 1
+#endif
 // gradient tiles staged through LDS and written as whole 128-byte row segments
 // with streaming stores (1), or stored from the accumulator layout (0)
 #ifndef BWD_LDS_EPI
@@ -148,8 +153,9 @@ struct DqTile {
 template <int D, bool CAUSAL, typename G>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    G* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH, float sl2, float scale) {
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ delta,
+    G* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH, float sl2, float scale,
+    const uint16_t* __restrict__ O, float* __restrict__ lse2_out) {
     using T = DqTile<D>;
     extern __shared__ __align__(16) uint16_t smem[];
     const int id = blockIdx.x;
@@ -174,7 +180,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const float lse_v = LSE[qrow];
     // rows with no visible key (lse = -inf) get P = 0
     const float lse2 = lse_v == kNegInf ? __builtin_huge_valf() : lse_v * kLog2e;
+#if BWD_FUSE_DELTA
+    // D = dO . O of this query row: O is read in the layout of the dO
+    // fragments (this lane's half of the row), the halves meet across lanes
+    // n and n + 32.  The row's D and lse2 go to the workspace for the dK/dV
+    // kernel, which runs after this one.
+    float dpart = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 of = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(O + qrow * D + kk * 16 + hf * 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)of[e], (float)df[kk][e], dpart);
+    }
+    const float dlt = dpart + __shfl_xor(dpart, 32, 64);
+    if (hf == 0 && qi < Nq) {
+        delta[qrow] = dlt;
+        lse2_out[qrow] = lse2;
+    }
+#else
     const float dlt = delta[qrow];
+#endif
 
     const uint16_t* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
     const uint16_t* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
@@ -813,10 +838,12 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
     const hipStream_t s = (hipStream_t)a.stream;
     const int rows = a.B * a.Hq * a.Nq;
     float* lse2 = a.delta + rows;
-    hipLaunchKernelGGL(bwd_delta_bf16_kernel<D>, dim3((rows * (D / 8) + 255) / 256), dim3(256), 0, s,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dO, a.lse, a.delta, lse2, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!BWD_FUSE_DELTA) {
+        hipLaunchKernelGGL(bwd_delta_bf16_kernel<D>, dim3((rows * (D / 8) + 255) / 256), dim3(256), 0, s,
+                           (const uint16_t*)a.o, (const uint16_t*)a.dO, a.lse, a.delta, lse2, rows);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const float sl2 = a.scale * kLog2e;
     {
         using T = DqTile<D>;
@@ -828,7 +855,7 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
-                           (G*)a.dq, a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, sl2, a.scale);
+                           (G*)a.dq, a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, sl2, a.scale, (const uint16_t*)a.o, lse2);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
