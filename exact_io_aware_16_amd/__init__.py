@@ -1,8 +1,11 @@
 """Python binding of libfa (exact IO-aware attention on MI355X / gfx950).
 
-Argument marshalling only: tensors are checked for device, dtype, shape and
-contiguity, their device pointers and torch's current HIP stream are passed to
-the C ABI (``include/fa.h``), and a non-zero status raises ``RuntimeError``.
+Argument marshalling only: every tensor's shape and dtype are checked against
+the others' (the C ABI sees only pointers and sizes, so a mismatch here would
+otherwise become an out-of-bounds device access), then device and contiguity;
+the device pointers and torch's current HIP stream are passed to the C ABI
+(``include/fa.h``), and a non-zero status raises ``RuntimeError``.  Shape
+mismatches raise ``ValueError``, dtype mismatches ``TypeError``.
 Every step of the computation runs in the HIP kernels of ``libfa.so``; there is
 no fallback of any kind.  PyTorch only provides device memory and streams.
 
@@ -99,6 +102,44 @@ def _dev(*tensors):
             raise ValueError("all tensors must be contiguous")
 
 
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _same_dtype(ref, *named):
+    for name, t in named:
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, expected {ref.dtype} (the dtype of q)")
+
+
+def _f32(t, name):
+    if t.dtype != _torch().float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+
+
+def _i32(t, name):
+    if t.dtype != _torch().int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+
+
+def _qkv(q, k, v, kname="k", vname="v"):
+    """q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d] of one shape; returns the sizes."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-d [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"{kname} {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dimension")
+    _shape(v, k.shape, vname)
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _workspace(ws):
+    if ws.dim() < 1:
+        raise ValueError("workspace must be a 1-d (or larger) tensor")
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -138,12 +179,16 @@ def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
     """Check and marshal the arguments of fa_fwd once; returns a zero-argument
     callable that launches it (the tensors must stay alive and unchanged in
     shape).  Raises on a non-zero status when called."""
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v)
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k", k), ("v", v), ("o", o))
+    _shape(o, q.shape, "o")
+    _f32(lse, "lse")
+    _shape(lse, (B, Hq, Nq), "lse")
     _dev(q, k, v, o, lse)
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nk, _ = k.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q), scale,
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, dcode, scale,
             int(bool(causal)), _stream(stream))
     return lambda: _check(lib.fa_fwd(*args))
 
@@ -151,15 +196,17 @@ def prepare_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
 def prepare_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, scale=None, stream=None):
     """fa_fwd_fp8's arguments checked and marshalled once.  q8, k8, v8 hold E4M3
     codes (torch.uint8 or torch.float8_e4m3fn); o is bfloat16."""
-    _dev(q8, k8, v8, o, lse)
     torch = _torch()
     codes = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
     if q8.dtype not in codes or k8.dtype not in codes or v8.dtype not in codes:
         raise TypeError("q8, k8, v8 must hold E4M3 codes (uint8 or float8_e4m3fn)")
     if o.dtype != torch.bfloat16:
         raise TypeError("o must be bfloat16")
-    B, Hq, Nq, d = q8.shape
-    _, Hkv, Nk, _ = k8.shape
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q8, k8, v8, "k8", "v8")
+    _shape(o, q8.shape, "o")
+    _f32(lse, "lse")
+    _shape(lse, (B, Hq, Nq), "lse")
+    _dev(q8, k8, v8, o, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     args = (_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, float(descale_q),
@@ -180,16 +227,27 @@ def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None):
 
 def prepare_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
     """fa_bwd's arguments checked and marshalled once (see prepare_fwd)."""
-    _dev(q, k, v, o, dO, lse, dq, dk, dv, workspace)
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nk, _ = k.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v)
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k", k), ("v", v), ("o", o), ("dO", dO))
+    _shape(o, q.shape, "o")
+    _shape(dO, q.shape, "dO")
+    _f32(lse, "lse")
+    _shape(lse, (B, Hq, Nq), "lse")
     gcode = _dtype_code(dq)
     if _dtype_code(dk) != gcode or _dtype_code(dv) != gcode:
         raise TypeError("dq, dk, dv must share one dtype")
+    if dcode == FA_F32 and gcode != FA_F32:
+        raise TypeError("float32 inputs give float32 gradients only")
+    _shape(dq, q.shape, "dq")
+    _shape(dk, k.shape, "dk")
+    _shape(dv, k.shape, "dv")
+    _workspace(workspace)
+    _dev(q, k, v, o, dO, lse, dq, dk, dv, workspace)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), gcode, B, Hq,
-            Hkv, Nq, Nk, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+            Hkv, Nq, Nk, d, dcode, scale, int(bool(causal)), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     return lambda: _check(lib.fa_bwd(*args))
 
@@ -201,16 +259,23 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, causal=False, scale=None,
 
 def prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
     """fa_decode's arguments checked and marshalled once (see prepare_fwd)."""
+    B, Hq, Hkv, one, Nmax, d = _qkv(q, k_cache, v_cache, "k_cache", "v_cache")
+    if one != 1:
+        raise ValueError(f"q must hold one token per head [B, Hq, 1, d], got {tuple(q.shape)}")
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k_cache", k_cache), ("v_cache", v_cache), ("o", o))
+    _shape(o, q.shape, "o")
+    _f32(lse, "lse")
+    if tuple(lse.shape) not in ((B, Hq), (B, Hq, 1)):
+        raise ValueError(f"lse has shape {tuple(lse.shape)}, expected {(B, Hq)}")
+    _i32(seqlens, "seqlens")
+    _shape(seqlens, (B,), "seqlens")
+    _workspace(workspace)
     _dev(q, k_cache, v_cache, seqlens, o, lse, workspace)
-    torch = _torch()
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
-    B, Hq, _, d = q.shape
-    _, Hkv, Nmax, _ = k_cache.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nmax, d,
-            _dtype_code(q), scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+            dcode, scale, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return lambda: _check(lib.fa_decode(*args))
 
 
@@ -221,16 +286,20 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, strea
 
 def prepare_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=True, scale=None, stream=None):
     """fa_decode_chunk's arguments checked and marshalled once (see prepare_fwd)."""
+    B, Hq, Hkv, Nq, Nmax, d = _qkv(q, k_cache, v_cache, "k_cache", "v_cache")
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k_cache", k_cache), ("v_cache", v_cache), ("o", o))
+    _shape(o, q.shape, "o")
+    _f32(lse, "lse")
+    _shape(lse, (B, Hq, Nq), "lse")
+    _i32(seqlens, "seqlens")
+    _shape(seqlens, (B,), "seqlens")
+    _workspace(workspace)
     _dev(q, k_cache, v_cache, seqlens, o, lse, workspace)
-    torch = _torch()
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nmax, _ = k_cache.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nmax, d,
-            _dtype_code(q), scale, int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            dcode, scale, int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
     return lambda: _check(lib.fa_decode_chunk(*args))
 
@@ -246,17 +315,30 @@ def prepare_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, work
                          stream=None):
     """fa_decode_paged's arguments checked and marshalled once (see prepare_fwd).
     k_pages/v_pages [num_pages, Hkv, page_size, d]; block_table [B, max_pages] int32."""
-    _dev(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace)
-    torch = _torch()
-    if seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise TypeError("seqlens and block_table must be int32")
+    if q.dim() != 4 or k_pages.dim() != 4:
+        raise ValueError("q [B, Hq, Nq, d] and k_pages [num_pages, Hkv, page_size, d] must be 4-d")
     B, Hq, Nq, d = q.shape
-    num_pages, Hkv, page_size, _ = k_pages.shape
+    num_pages, Hkv, page_size, dk = k_pages.shape
+    if dk != d:
+        raise ValueError(f"k_pages {tuple(k_pages.shape)} does not match q {tuple(q.shape)} in head dimension")
+    _shape(v_pages, k_pages.shape, "v_pages")
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k_pages", k_pages), ("v_pages", v_pages), ("o", o))
+    _shape(o, q.shape, "o")
+    _f32(lse, "lse")
+    _shape(lse, (B, Hq, Nq), "lse")
+    _i32(seqlens, "seqlens")
+    _shape(seqlens, (B,), "seqlens")
+    _i32(block_table, "block_table")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages], got {tuple(block_table.shape)}")
     max_pages = block_table.shape[1]
+    _workspace(workspace)
+    _dev(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     args = (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq,
-            Hkv, Nq, num_pages, page_size, max_pages, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+            Hkv, Nq, num_pages, page_size, max_pages, d, dcode, scale, int(bool(causal)), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     return lambda: _check(lib.fa_decode_paged(*args))
 

@@ -37,7 +37,7 @@ const char* fa_status_str(int status) {
         case FA_OK: return "FA_OK";
         case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (size < 1, Hq % Hkv != 0, causal with Nq > Nk, or tensor too large)";
-        case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype, or bfloat16 gradients of float32 inputs";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
         case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
@@ -78,6 +78,8 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
     if (too_big(B, Hq, Nq, d) || too_big(B, Hkv, Nk, d)) return FA_ERR_SHAPE;
     if ((dtype != FA_F32 && dtype != FA_BF16) || (grad_dtype != FA_F32 && grad_dtype != FA_BF16))
         return FA_ERR_DTYPE;
+    // float32 inputs produce float32 gradients only
+    if (dtype == FA_F32 && grad_dtype != FA_F32) return FA_ERR_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
     if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;

@@ -849,10 +849,8 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
         using T = DqTile<D>;
         const int nqb = (a.Nq + T::BM - 1) / T::BM;
         const int BH = a.B * a.Hq;
-        auto kern = bwd_dq_kernel<D, CAUSAL, G>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                T::LDS_BYTES);
-        if (e != hipSuccess) return e;
+        constexpr auto kern = bwd_dq_kernel<D, CAUSAL, G>;
+        if ((e = ensure_dynamic_lds<kern>(T::LDS_BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
                            (G*)a.dq, a.Hq, a.Hkv, a.Nq, a.Nk, nqb, BH, sl2, a.scale, (const uint16_t*)a.o, lse2);
@@ -862,10 +860,8 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
     {
         using T = DkvTile<D>;
         const int nkb = (a.Nk + T::BK - 1) / T::BK;
-        auto kern = bwd_dkdv_kernel<D, CAUSAL, G>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                T::LDS_BYTES);
-        if (e != hipSuccess) return e;
+        constexpr auto kern = bwd_dkdv_kernel<D, CAUSAL, G>;
+        if ((e = ensure_dynamic_lds<kern>(T::LDS_BYTES)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(nkb * a.B * a.Hkv), dim3(256), T::LDS_BYTES, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, lse2, a.delta,
                            (G*)a.dk, (G*)a.dv, a.Hq, a.Hkv, a.Nq, a.Nk, a.B * a.Hkv, sl2, a.scale);
@@ -899,8 +895,7 @@ static hipError_t launch_bwd_f32_d(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a) {
-    // float32 gradients only for float32 inputs
-    if (a.grad_bf16) return hipErrorNotSupported;
+    // float32 gradients only (bfloat16 ones are rejected by the ABI layer)
     return a.d == 64 ? launch_bwd_f32_d<64>(a) : launch_bwd_f32_d<128>(a);
 }
 

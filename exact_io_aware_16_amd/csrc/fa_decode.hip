@@ -498,15 +498,11 @@ __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
 template <int D, int QR>
 static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
     using T = StreamTile<D, DEC_STAGES, QR>;
-    auto kern = decode_stream_kernel<D, DEC_STAGES, QR>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    constexpr auto kern = decode_stream_kernel<D, DEC_STAGES, QR>;
+    hipError_t e = ensure_dynamic_lds<kern>(T::LDS_BYTES);
     if (e != hipSuccess) return e;
-    int dev = 0, ncu = 0, lds = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
-        return e;
+    int ncu = 0, lds = 0;
+    if ((e = device_caps(&ncu, &lds)) != hipSuccess) return e;
     // as many one-wave workgroups as the LDS of all CUs holds at once
     const int per_cu = std::max(1, std::min(8, lds / T::LDS_BYTES));
     const int G = std::max(2, std::min(kDecodeMaxWaves, ncu * per_cu) & ~1);   // even (pairs)

@@ -534,9 +534,8 @@ static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
     using T = RingTile<D, NW, S, NT>;
     const int nqb = (a.Nq + T::BM - 1) / T::BM;
     const int BH = a.B * a.Hq;
-    auto kern = fwd_ring_kernel<D, NW, S, NT, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    constexpr auto kern = fwd_ring_kernel<D, NW, S, NT, CAUSAL>;
+    const hipError_t e = ensure_dynamic_lds<kern>(T::LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
@@ -549,8 +548,8 @@ static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
 // (workgroups of 256 queries, 2 per CU) to fill the chip past the causal tail;
 // smaller grids keep one tile per wave (more, lighter workgroups).
 static bool fwd64_two_tiles(const FwdArgs& a) {
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int ncu = 256, lds = 0;
+    if (device_caps(&ncu, &lds) != hipSuccess) ncu = 256;
     using T2 = RingTile<64, RING_NW64, RING_S64, 2>;
     const long long wgs = (long long)((a.Nq + T2::BM - 1) / T2::BM) * a.B * a.Hq;
     return wgs >= (long long)(a.causal ? 4 : 2) * ncu;

@@ -311,9 +311,8 @@ hipError_t launch_fp8_t(const Fp8Args& a) {
     using T = Fp8Tile<D, NW, S>;
     const int nqb = (a.Nq + T::BM - 1) / T::BM;
     const int BH = a.B * a.Hq;
-    auto kern = fwd_fp8_kernel<D, NW, S, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    constexpr auto kern = fwd_fp8_kernel<D, NW, S, CAUSAL>;
+    const hipError_t e = ensure_dynamic_lds<kern>(T::LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(NW * 64), T::LDS_BYTES, (hipStream_t)a.stream,
                        (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq,

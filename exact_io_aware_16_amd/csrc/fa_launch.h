@@ -5,7 +5,63 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace fa {
+
+// ---------------------------------------------------------------------------
+// Per-device facts and kernel attributes, looked up once per process.  The
+// runtime calls behind them (attribute queries, hipFuncSetAttribute) are host
+// work that every launch would otherwise repeat.  Devices numbered at or past
+// kMaxDevices are served without the cache.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+
+// Compute units and bytes of LDS per compute unit of the current device.
+inline hipError_t device_caps(int* ncu, int* lds_per_cu) {
+    static std::atomic<int> cu_cache[kMaxDevices];
+    static std::atomic<int> lds_cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached) {
+        const int c = cu_cache[dev].load(std::memory_order_relaxed);
+        const int l = lds_cache[dev].load(std::memory_order_relaxed);
+        if (c > 0 && l > 0) {
+            *ncu = c;
+            *lds_per_cu = l;
+            return hipSuccess;
+        }
+    }
+    int c = 0, l = 0;
+    if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
+        return e;
+    if (cached) {
+        cu_cache[dev].store(c, std::memory_order_relaxed);
+        lds_cache[dev].store(l, std::memory_order_relaxed);
+    }
+    *ncu = c;
+    *lds_per_cu = l;
+    return hipSuccess;
+}
+
+// Raise the dynamic-LDS limit of kernel Kern to `bytes` on the current device,
+// the first time it is launched there (every instantiation keeps its own mask
+// of the devices already set up; a repeat of the call is harmless).
+template <auto Kern>
+hipError_t ensure_dynamic_lds(int bytes) {
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = (dev >= 0 && dev < kMaxDevices) ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // A paged K/V cache: pools [num_pages][Hkv][page_size][d]; key j of sequence
 // b is row j % page_size of page table[b * max_pages + j / page_size] (entries

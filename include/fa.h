@@ -35,9 +35,12 @@
  * - stream is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on that stream and returns; nothing is synchronised.
  * - Ownership: the caller allocates and owns every buffer, workspaces
- *   included.  The library allocates nothing, frees nothing, keeps no pointer
- *   after returning, and holds no mutable global state, so calls on different
- *   streams are independent.  Outputs are fully overwritten.
+ *   included.  The library allocates nothing, frees nothing and keeps no
+ *   pointer after returning.  Its only global state is a per-device cache of
+ *   facts looked up on first use (compute-unit count, LDS size, each kernel's
+ *   dynamic-LDS attribute), filled idempotently and safe to race on, so calls
+ *   on different streams or threads are independent.  Outputs are fully
+ *   overwritten.
  * - Errors: host-visible arguments are checked before anything is enqueued;
  *   on any error nothing is launched and a status != FA_OK is returned.  A
  *   failed kernel launch returns FA_ERR_HIP.  No exception crosses the ABI.
@@ -58,7 +61,8 @@ typedef enum {
     FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                      */
     FA_ERR_SHAPE = 2,        /* a size < 1, Hq % Hkv != 0, causal with Nq > Nk,  */
                              /* or a tensor above 2^31 elements                  */
-    FA_ERR_DTYPE = 3,        /* dtype / grad_dtype not one of fa_dtype_t         */
+    FA_ERR_DTYPE = 3,        /* dtype / grad_dtype not one of fa_dtype_t, or     */
+                             /* FA_BF16 gradients asked of FA_F32 inputs         */
     FA_ERR_UNSUPPORTED = 4,  /* head dimension d other than 64 or 128           */
     FA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the query says    */
     FA_ERR_HIP = 6,          /* the HIP runtime refused a launch                 */
@@ -93,7 +97,9 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
  * Backward pass: gradients of sum(O * dO) with respect to q, k, v.
  *   q, k, v, o (the forward output), dO in dtype, lse from fa_fwd;
  *   dq [B,Hq,Nq,d], dk/dv [B,Hkv,Nk,d] written in grad_dtype (FA_F32 is the
- *   default choice; FA_BF16 rounds the float32 result to bfloat16).  With
+ *   default choice; FA_BF16 rounds the float32 result to bfloat16 and is
+ *   accepted for FA_BF16 inputs only: FA_F32 inputs with FA_BF16 gradients
+ *   return FA_ERR_DTYPE).  With
  *   grouped heads, dk/dv of a K/V head are the sums over its query heads.
  *   The result is deterministic (no atomics): repeated calls give the same bits.
  *   workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes.

@@ -415,9 +415,19 @@ def merge_partials(o_parts, lse_parts):
 # ---------------------------------------------------------------------------
 
 def compare(gpu, ref):
-    """max-abs and rel-L2 in float64 over the whole array (finite entries of ref)."""
+    """max-abs and rel-L2 in float64 over the whole array.
+
+    max_abs = max |gpu - ref| and rel_l2 = ||gpu - ref||_2 / ||ref||_2 over the
+    finite entries of ref (the absolute ||gpu - ref||_2 when ref is all zero).
+    Non-finite entries of ref (LSE = -inf of rows that see no key) must be
+    matched exactly by gpu, and gpu must be finite wherever ref is: otherwise
+    the result is flagged ``nonfinite_mismatch`` with both metrics infinite.
+    A NaN anywhere is a mismatch.  Arrays of different shapes raise ValueError.
+    """
     g = _f64(gpu)
     r = _f64(ref)
+    if g.shape != r.shape:
+        raise ValueError(f"compare: shapes differ {g.shape} vs {r.shape}")
     fin = np.isfinite(r)
     if not np.array_equal(np.isfinite(g), fin):
         return {"max_abs": float("inf"), "rel_l2": float("inf"), "nonfinite_mismatch": True}

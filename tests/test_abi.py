@@ -98,6 +98,9 @@ def test_bwd_validation(lib):
     assert bwd(Hq=3, Hkv=2) == 2
     assert bwd(ws=N) == 5
     assert bwd(wsb=4 * 8 * 2 - 1) == 5
+    # float32 inputs give float32 gradients only: bf16 ones are refused on the host
+    assert bwd(dtype=0, grad=1) == 3
+    assert "float32" in lib.fa_status_str(3).decode()
 
 
 def test_decode_validation(lib):
@@ -174,3 +177,91 @@ def test_one_hip_runtime_in_the_process(lib):
     maps = open("/proc/self/maps").read().splitlines()
     hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+# ---------------------------------------------------------------------------
+# the binding checks every tensor's shape and dtype against the others before
+# anything reaches the C ABI (which sees only pointers and sizes); CPU tensors
+# are enough, since these checks come before the device check
+# ---------------------------------------------------------------------------
+
+def test_binding_rejects_mismatched_tensors(lib):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    z = lambda *shape, dt=bf: torch.zeros(*shape, dtype=dt)
+    q, k, o, lse = z(2, 4, 8, 64), z(2, 2, 8, 64), z(2, 4, 8, 64), z(2, 4, 8, dt=f32)
+    # forward
+    with pytest.raises(ValueError, match="v has shape"):
+        fa.prepare_fwd(q, k, z(2, 2, 9, 64), o, lse)
+    with pytest.raises(ValueError, match="batch or head dimension"):
+        fa.prepare_fwd(q, z(1, 2, 8, 64), z(1, 2, 8, 64), o, lse)
+    with pytest.raises(ValueError, match="batch or head dimension"):
+        fa.prepare_fwd(q, z(2, 2, 8, 128), z(2, 2, 8, 128), o, lse)
+    with pytest.raises(TypeError, match="k is"):
+        fa.prepare_fwd(q.float(), k, k, o.float(), lse)
+    with pytest.raises(TypeError, match="o is"):
+        fa.prepare_fwd(q, k, k, o.float(), lse)
+    with pytest.raises(ValueError, match="o has shape"):
+        fa.prepare_fwd(q, k, k, z(2, 4, 7, 64), lse)
+    with pytest.raises(ValueError, match="lse has shape"):
+        fa.prepare_fwd(q, k, k, o, z(2, 4, 7, dt=f32))
+    with pytest.raises(TypeError, match="lse must be float32"):
+        fa.prepare_fwd(q, k, k, o, z(2, 4, 8))
+    with pytest.raises(ValueError, match="on the GPU"):   # well formed: stops at the device check
+        fa.prepare_fwd(q, k, k, o, lse)
+    # backward
+    g32 = lambda t: torch.zeros(t.shape, dtype=f32)
+    ws = z(1024, dt=torch.uint8)
+    with pytest.raises(ValueError, match="dq has shape"):
+        fa.prepare_bwd(q, k, k, o, o, lse, z(2, 4, 8, 32, dt=f32), g32(k), g32(k), ws)
+    with pytest.raises(ValueError, match="dk has shape"):
+        fa.prepare_bwd(q, k, k, o, o, lse, g32(q), g32(q), g32(k), ws)
+    with pytest.raises(ValueError, match="dO has shape"):
+        fa.prepare_bwd(q, k, k, o, z(2, 4, 9, 64), lse, g32(q), g32(k), g32(k), ws)
+    with pytest.raises(TypeError, match="dO is"):
+        fa.prepare_bwd(q, k, k, o, o.float(), lse, g32(q), g32(k), g32(k), ws)
+    with pytest.raises(TypeError, match="share one dtype"):
+        fa.prepare_bwd(q, k, k, o, o, lse, g32(q), g32(k).to(bf), g32(k), ws)
+    with pytest.raises(TypeError, match="float32 gradients only"):
+        fa.prepare_bwd(q.float(), k.float(), k.float(), o.float(), o.float(), lse, q, k, k, ws)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fa.prepare_bwd(q, k, k, o, o, lse, g32(q), g32(k), g32(k), ws)
+    # decode and chunk decode
+    qd, kc, od = z(3, 8, 1, 128), z(3, 2, 100, 128), z(3, 8, 1, 128)
+    sl, ld = torch.zeros(3, dtype=torch.int32), z(3, 8, dt=f32)
+    with pytest.raises(ValueError, match="seqlens has shape"):
+        fa.prepare_decode(qd, kc, kc, sl[:2], od, ld, ws)
+    with pytest.raises(TypeError, match="seqlens must be int32"):
+        fa.prepare_decode(qd, kc, kc, sl.long(), od, ld, ws)
+    with pytest.raises(ValueError, match="one token per head"):
+        fa.prepare_decode(z(3, 8, 2, 128), kc, kc, sl, z(3, 8, 2, 128), ld, ws)
+    with pytest.raises(ValueError, match="lse has shape"):
+        fa.prepare_decode(qd, kc, kc, sl, od, z(3, 4, dt=f32), ws)
+    with pytest.raises(ValueError, match="v_cache has shape"):
+        fa.prepare_decode(qd, kc, z(3, 2, 99, 128), sl, od, ld, ws)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fa.prepare_decode(qd, kc, kc, sl, od, ld, ws)
+    qc = z(3, 8, 4, 128)
+    with pytest.raises(ValueError, match="lse has shape"):
+        fa.prepare_decode_chunk(qc, kc, kc, sl, qc.clone(), ld, ws)
+    with pytest.raises(ValueError, match="seqlens has shape"):
+        fa.prepare_decode_chunk(qc, kc, kc, sl[:1], qc.clone(), z(3, 8, 4, dt=f32), ws)
+    # paged decode
+    kp, bt = z(10, 2, 64, 128), torch.zeros(3, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="block_table must be"):
+        fa.prepare_decode_paged(qc, kp, kp, bt[:2], sl, qc.clone(), z(3, 8, 4, dt=f32), ws)
+    with pytest.raises(TypeError, match="block_table must be int32"):
+        fa.prepare_decode_paged(qc, kp, kp, bt.long(), sl, qc.clone(), z(3, 8, 4, dt=f32), ws)
+    with pytest.raises(ValueError, match="head dimension"):
+        fa.prepare_decode_paged(qc, z(10, 2, 64, 64), z(10, 2, 64, 64), bt, sl, qc.clone(), z(3, 8, 4, dt=f32), ws)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fa.prepare_decode_paged(qc, kp, kp, bt, sl, qc.clone(), z(3, 8, 4, dt=f32), ws)
+    # fp8 forward
+    u8 = torch.uint8
+    q8, k8 = z(2, 4, 8, 64, dt=u8), z(2, 2, 8, 64, dt=u8)
+    with pytest.raises(ValueError, match="v8 has shape"):
+        fa.prepare_fwd_fp8(q8, k8, z(2, 2, 7, 64, dt=u8), o, lse, 1.0, 1.0, 1.0)
+    with pytest.raises(ValueError, match="lse has shape"):
+        fa.prepare_fwd_fp8(q8, k8, k8, o, z(2, 4, dt=f32), 1.0, 1.0, 1.0)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fa.prepare_fwd_fp8(q8, k8, k8, o, lse, 1.0, 1.0, 1.0)

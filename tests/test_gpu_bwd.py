@@ -116,25 +116,20 @@ def test_backward_beyond_2gib():
     """64 heads of 200000 queries against 64 keys each, d = 128, non-causal: Q,
     dO and O are 3.3 GB and dQ (float32) 6.6 GB, so byte offsets pass 2^31.
     Inputs come from an integer hash of their indices, built on the GPU and
-    re-derived on the host; the fp64 oracle checks dK and dV of two whole heads
-    (the last among them) and dQ on sampled rows of those heads, the last rows
-    included.
+    re-derived on the host; the fp64 oracle (ref_bwd) checks dK and dV of two
+    whole heads (the last among them) and dQ on sampled rows of those heads,
+    the last rows included.
 
-    Tolerance: each dK and dV element sums 200000 terms of random sign, so both
-    the sum and the error of the bf16-rounded P and dS operands (2^-9 relative
-    each) grow like the square root of the count: the relative error in norm
-    stays at the bf16 level (rel-L2 <= 5e-3) while an absolute max-abs bound
-    does not, so max-abs is taken relative to the largest reference value
-    (<= 2e-2 of it).  dQ rows are 64-term sums: the usual bf16 tolerance."""
+    Magnitude: each dK and dV element sums 200000 terms, so with dO of the
+    hash's size (|x| < 2) the gradients reach ~80 and the absolute bf16 bound
+    would be a relative one of 2.5e-4.  dO is therefore the hash times 2^-6
+    (exact in bf16; the gradients are linear in dO, so this scales results and
+    rounding errors alike by 2^-6), which puts the gradients at the size the
+    configurations' N(0,1) inputs give (|grad| up to ~2), and the usual
+    absolute bf16 tolerance applies unchanged."""
     import torch
     H, Nq, Nk, d = 64, 200_000, 64, 128
-
-    def close(name, gpu, ref):
-        err = np.abs(gpu - ref).max()
-        rel = np.linalg.norm(gpu - ref) / np.linalg.norm(ref)
-        print(f"  {name}: max_abs={err:.3e} (max |ref| {np.abs(ref).max():.3e}) rel_l2={rel:.3e}", flush=True)
-        assert err <= 2e-2 * np.abs(ref).max() and rel <= 5e-3, (name, err, rel)
-
+    do_scale = 2.0 ** -6
     announce(f"backward with Q, dO, O of {H * Nq * d * 2 / 2**30:.1f} GiB each")
     dev = "cuda:0"
     cols = torch.arange(d, device=dev, dtype=torch.int64)[None, :]
@@ -146,26 +141,21 @@ def test_backward_beyond_2gib():
     v = torch.empty_like(k)
     for h in range(H):
         q[0, h] = W.hash_values(rows + h * Nq, cols, 3).to(torch.bfloat16)
-        do[0, h] = W.hash_values(rows + h * Nq, cols, 4).to(torch.bfloat16)
+        do[0, h] = (W.hash_values(rows + h * Nq, cols, 4) * do_scale).to(torch.bfloat16)
         k[0, h] = W.hash_values(keys + h * Nk, cols, 1).to(torch.bfloat16)
         v[0, h] = W.hash_values(keys + h * Nk, cols, 2).to(torch.bfloat16)
     o, lse = fa.fwd(q, k, v, causal=False)
     dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=False)
     torch.cuda.synchronize()
-    scale = 1.0 / np.sqrt(d)
     colsn = np.arange(d, dtype=np.int64)[None, :]
     for h in (5, H - 1):
         qn = W.hash_values(np.arange(Nq, dtype=np.int64)[:, None] + h * Nq, colsn, 3)
-        don = W.hash_values(np.arange(Nq, dtype=np.int64)[:, None] + h * Nq, colsn, 4)
+        don = W.hash_values(np.arange(Nq, dtype=np.int64)[:, None] + h * Nq, colsn, 4) * do_scale
         kn = W.hash_values(np.arange(Nk, dtype=np.int64)[:, None] + h * Nk, colsn, 1)
         vn = W.hash_values(np.arange(Nk, dtype=np.int64)[:, None] + h * Nk, colsn, 2)
-        s = scale * (qn @ kn.T)
-        p = np.exp(s - s.max(axis=1, keepdims=True))
-        p /= p.sum(axis=1, keepdims=True)
-        dp = don @ vn.T
-        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-        close(f"dK[h={h}]", to_host(dk[0, h]), scale * (ds.T @ qn))
-        close(f"dV[h={h}]", to_host(dv[0, h]), p.T @ don)
+        dQ, dK, dV = oracle.ref_bwd(qn[None, None], kn[None, None], vn[None, None], don[None, None], causal=False)
+        print(f"  head {h}: max |dK| {np.abs(dK).max():.3f}, max |dV| {np.abs(dV).max():.3f}", flush=True)
+        assert_close(f"dK[h={h}]", to_host(dk[0, h]), dK[0, 0], TOL_BF16)
+        assert_close(f"dV[h={h}]", to_host(dv[0, h]), dV[0, 0], TOL_BF16)
         sel = np.r_[np.random.Generator(np.random.PCG64(h)).integers(0, Nq, 256), np.arange(Nq - 8, Nq)]
-        dQ = scale * (ds[sel] @ kn)
-        assert_close(f"dQ[h={h}, rows]", to_host(dq[0, h][torch.from_numpy(sel).to(dev)]), dQ, TOL_BF16)
+        assert_close(f"dQ[h={h}, rows]", to_host(dq[0, h][torch.from_numpy(sel).to(dev)]), dQ[0, 0][sel], TOL_BF16)

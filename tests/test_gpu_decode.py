@@ -161,26 +161,21 @@ def test_decode_cache_beyond_2gib():
     o, lse = to_host(o)[0, :, 0], to_host(lse)[0]
     del k, v
     torch.cuda.empty_cache()
-    # oracle: exact softmax over all N keys, streamed in chunks with a running max
-    scale = 1.0 / np.sqrt(d)
-    m = np.full(Hq, -np.inf); l = np.zeros(Hq); acc = np.zeros((Hq, d))
+    # oracle: the definition (ref_fwd) on each chunk of 2^20 keys, the chunks'
+    # (O, LSE) pairs merged by merge_partials (pinned: a split merged equals
+    # the unsplit result); the host never holds more than one chunk
     colsn = np.arange(d, dtype=np.int64)[None, :]
     pool = ThreadPoolExecutor(8)
 
     def gen(j, salt):   # the hash of one chunk of keys, its rows split over threads
         return np.concatenate(list(pool.map(lambda b: W.hash_values(b, colsn, salt), np.array_split(j, 8))))
+    parts_o, parts_l = [], []
     for j0 in range(0, N, chunk):
         j = np.arange(j0, min(N, j0 + chunk), dtype=np.int64)[:, None]
-        kc, vc = gen(j, 1), gen(j, 2)
-        s = scale * (qv @ kc.T)                     # [Hq, chunk]
-        mn = np.maximum(m, s.max(axis=1))
-        c = np.exp(m - mn)
-        e = np.exp(s - mn[:, None])
-        l = l * c + e.sum(axis=1)
-        acc = acc * c[:, None] + e @ vc
-        m = mn
+        Oc, Lc = oracle.ref_fwd(qv[None, :, None, :], gen(j, 1)[None, None], gen(j, 2)[None, None], causal=False)
+        parts_o.append(Oc[0, :, 0])
+        parts_l.append(Lc[0, :, 0])
     pool.shutdown()
-    O = acc / l[:, None]
-    L = m + np.log(l)
+    O, L = oracle.merge_partials(np.stack(parts_o), np.stack(parts_l))
     assert_close("O", o, O, TOL_BF16)
     assert_close("LSE", lse, L, TOL_BF16)

@@ -315,3 +315,80 @@ def test_unmutated_fp8_oracle_passes():
 @pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
 def test_fp8_mutant_is_caught(name):
     assert _some_check_fails(_fp8_checks(*FP8_MUTANTS[name])), f"mutant {name} passed every pin"
+
+
+# ref_fwd_rows: slips in the per-row key range or the head map
+def _rows_mutant(limit, head=None):
+    def rows_fn(q, k, v, rows, causal, scale):
+        B, Hq, Nq, d = np.shape(q)
+        Hkv, Nk = np.shape(k)[1], np.shape(k)[2]
+        O = np.zeros((len(rows), d)); L = np.full(len(rows), -np.inf)
+        for r, (b, h, i) in enumerate(rows):
+            g = head(h, Hq, Hkv) if head else h // (Hq // Hkv)
+            hi = max(0, min(Nk, limit(i, Nq, Nk))) if causal else Nk
+            if hi == 0:
+                continue
+            s = scale * (k[b, g, :hi] @ q[b, h, i])
+            e = np.exp(s - s.max())
+            O[r] = e @ v[b, g, :hi] / e.sum(); L[r] = s.max() + np.log(e.sum())
+        return O, L
+    return rows_fn
+
+
+ROWS_MUTANTS = {
+    "rows_offset_sign_flipped": _rows_mutant(lambda i, Nq, Nk: i - (Nk - Nq) + 1),
+    "rows_diagonal_key_dropped": _rows_mutant(lambda i, Nq, Nk: i + (Nk - Nq)),
+    "rows_top_left_aligned": _rows_mutant(lambda i, Nq, Nk: i + 1),
+    "rows_head_map_interleaved": _rows_mutant(lambda i, Nq, Nk: i + (Nk - Nq) + 1, head=lambda h, Hq, Hkv: h % Hkv),
+}
+
+
+def test_unmutated_rows_oracle_passes():
+    assert pins.check_rows_variant(pins.rows_oracle)
+    # the mutant scaffold itself, with the right range and head map, passes too
+    assert pins.check_rows_variant(_rows_mutant(lambda i, Nq, Nk: i + (Nk - Nq) + 1))
+
+
+@pytest.mark.parametrize("name", sorted(ROWS_MUTANTS))
+def test_rows_mutant_is_caught(name):
+    assert not pins.check_rows_variant(ROWS_MUTANTS[name]), f"mutant {name} passed the pin"
+
+
+# compare: a wrong norm, a signed maximum, the wrong denominator, a lost
+# non-finite check
+def _cmp_mutant(kind):
+    def cmp(gpu, ref):
+        g, r = np.asarray(gpu, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+        if g.shape != r.shape:
+            raise ValueError("shape")
+        fin = np.isfinite(r)
+        if kind != "nonfinite_ignored":
+            if not np.array_equal(np.isfinite(g), fin) or not np.array_equal(g[~fin], r[~fin]):
+                return {"max_abs": np.inf, "rel_l2": np.inf, "nonfinite_mismatch": True}
+        diff = g[fin] - r[fin]
+        nr = np.linalg.norm(r[fin])
+        mx = float(np.abs(diff).max()) if diff.size else 0.0
+        if kind == "signed_max":
+            mx = float(diff.max()) if diff.size else 0.0
+        num = np.linalg.norm(diff)
+        if kind == "l1_norm":
+            num, nr = np.abs(diff).sum(), np.abs(r[fin]).sum()
+        if kind == "squared_ratio":
+            num, nr = num ** 2, nr ** 2
+        if kind == "relative_to_result":
+            nr = np.linalg.norm(g[fin])
+        return {"max_abs": mx, "rel_l2": float(num / nr) if nr > 0 else float(num)}
+    return cmp
+
+
+COMPARE_MUTANTS = ["signed_max", "l1_norm", "squared_ratio", "relative_to_result", "nonfinite_ignored"]
+
+
+def test_unmutated_compare_scaffold_passes():
+    assert pins.check_compare(_cmp_mutant("none"))
+
+
+@pytest.mark.parametrize("name", COMPARE_MUTANTS)
+def test_compare_mutant_is_caught(name):
+    with np.errstate(all="ignore"):
+        assert not pins.check_compare(_cmp_mutant(name)), f"mutant {name} passed the pin"

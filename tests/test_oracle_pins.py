@@ -286,6 +286,119 @@ def test_rows_variant_matches_full():
             assert abs(Lr[r] - L[b, h, i]) <= 1e-12
 
 
+# ---------------------------------------------------------------------------
+# ref_fwd_rows: the definition one query row at a time (sampled-row parity of
+# the large workloads), checked against pure-Python brute force on causal
+# shapes with Nq < Nk (bottom-right offset Nk - Nq > 0) and grouped heads
+# ---------------------------------------------------------------------------
+
+def check_rows_variant(rows_fn):
+    """rows_fn(q, k, v, rows, causal, scale) -> (O [R, d], LSE [R])."""
+    ok = True
+    for seed, (B, Hq, Hkv, Nq, Nk, d, causal) in enumerate([
+            (2, 4, 2, 3, 7, 3, True),     # offset 4, two query heads per K/V head
+            (1, 6, 3, 5, 5, 2, True),     # Nq == Nk
+            (1, 4, 1, 2, 9, 3, True),     # offset 7, one K/V head for all
+            (2, 4, 2, 4, 6, 2, False)]):
+        q = _rand(seed + 300, B, Hq, Nq, d)
+        k, v = _rand(seed + 310, B, Hkv, Nk, d), _rand(seed + 320, B, Hkv, Nk, d)
+        Ob, Lb = brute_attention(q, k, v, causal, 0.6)
+        rows = np.array([[b, h, i] for b in range(B) for h in range(Hq) for i in range(Nq)])
+        Or, Lr = rows_fn(q, k, v, rows, causal, 0.6)
+        for r, (b, h, i) in enumerate(rows):
+            ok &= np.abs(Or[r] - Ob[b, h, i]).max() <= 1e-12 and abs(Lr[r] - Lb[b, h, i]) <= 1e-12
+    return bool(ok)
+
+
+def rows_oracle(q, k, v, rows, causal, scale):
+    return oracle.ref_fwd_rows(q, k, v, rows, causal=causal, scale=scale)
+
+
+def test_rows_variant_brute_force_offset_and_groups():
+    assert check_rows_variant(rows_oracle)
+
+
+def test_rows_variant_matches_full_bottom_right_gqa():
+    """Nq < Nk causal with grouped heads: every sampled row equals ref_fwd's."""
+    w = random_case(4, 2, 8, 2, 24, 61, 16, dtype="f32")
+    q, k, v = w.values("q"), w.values("k"), w.values("v")
+    O, L = oracle.ref_fwd(q, k, v, causal=True)
+    rows = np.array([[b, h, i] for b in range(2) for h in (0, 3, 4, 7) for i in (0, 1, 11, 23)])
+    Or, Lr = oracle.ref_fwd_rows(q, k, v, rows, causal=True)
+    for r, (b, h, i) in enumerate(rows):
+        assert np.abs(Or[r] - O[b, h, i]).max() <= 1e-12
+        assert abs(Lr[r] - L[b, h, i]) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# compare: the metric behind every parity test
+# ---------------------------------------------------------------------------
+
+def _brute_metrics(g, r):
+    """max |g - r| and ||g - r|| / ||r|| by plain Python loops over finite r."""
+    mx, num, den = 0.0, 0.0, 0.0
+    for a, b in zip(np.ravel(g).tolist(), np.ravel(r).tolist()):
+        if math.isfinite(b):
+            mx = max(mx, abs(a - b))
+            num += (a - b) ** 2
+            den += b * b
+    return mx, math.sqrt(num) / math.sqrt(den)
+
+
+def check_compare(cmp):
+    ok = True
+    mism = lambda m: bool(m.get("nonfinite_mismatch"))
+    # hand-built: ref norm 5, difference (0, 0.5)
+    m = cmp(np.array([3.0, 4.5]), np.array([3.0, 4.0]))
+    ok &= m["max_abs"] == 0.5 and abs(m["rel_l2"] - 0.1) < 1e-15 and not mism(m)
+    # the largest deviation is negative; difference norm 0.5, ref norm 10
+    r = np.ones(100)
+    g = r.copy()
+    g[3] += 0.3
+    g[70] -= 0.4
+    m = cmp(g, r)
+    ok &= abs(m["max_abs"] - 0.4) < 1e-15 and abs(m["rel_l2"] - 0.05) < 1e-15
+    # relative to the reference's norm, not the result's (g = 2r: rel-L2 = 1)
+    m = cmp(np.array([6.0, 8.0]), np.array([3.0, 4.0]))
+    ok &= m["max_abs"] == 4.0 and abs(m["rel_l2"] - 1.0) < 1e-15
+    # equal arrays, any shape
+    r = _rand(5, 3, 4, 5)
+    m = cmp(r.copy(), r)
+    ok &= m["max_abs"] == 0.0 and m["rel_l2"] == 0.0
+    # brute force on random 3-d arrays
+    g = r + 1e-3 * _rand(6, 3, 4, 5)
+    mx, rel = _brute_metrics(g, r)
+    m = cmp(g, r)
+    ok &= abs(m["max_abs"] - mx) < 1e-15 and abs(m["rel_l2"] - rel) < 1e-13
+    # -inf in the same places (rows without keys) is equal and left out of the norms
+    m = cmp(np.array([-np.inf, 2.5, -np.inf]), np.array([-np.inf, 2.0, -np.inf]))
+    ok &= m["max_abs"] == 0.5 and m["rel_l2"] == 0.25 and not mism(m)
+    # a whole row of -inf on both sides
+    m = cmp(np.full(4, -np.inf), np.full(4, -np.inf))
+    ok &= m["max_abs"] == 0.0 and m["rel_l2"] == 0.0 and not mism(m)
+    # non-finite patterns that differ, either way, and +inf for -inf
+    for g2, r2 in ([0.0, 1.0], [-np.inf, 1.0]), ([-np.inf, 1.0], [0.0, 1.0]), ([np.inf, 1.0], [-np.inf, 1.0]):
+        m = cmp(np.array(g2), np.array(r2))
+        ok &= mism(m) and m["max_abs"] == np.inf and m["rel_l2"] == np.inf
+    # NaN in the result fails, also where the reference is -inf
+    for g2, r2 in ([np.nan, 1.0], [0.0, 1.0]), ([np.nan, 1.0], [-np.inf, 1.0]):
+        ok &= mism(cmp(np.array(g2), np.array(r2)))
+    # an all-zero reference: rel-L2 is the absolute norm of the difference
+    m = cmp(np.array([0.0, 3e-3, 4e-3]), np.zeros(3))
+    ok &= m["max_abs"] == 4e-3 and abs(m["rel_l2"] - 5e-3) < 1e-15
+    # arrays of different shapes are an error, not a silent broadcast
+    try:
+        cmp(np.zeros((2, 3)), np.zeros(3))
+        ok = False
+    except ValueError:
+        pass
+    return bool(ok)
+
+
+def test_compare_metrics():
+    assert check_compare(oracle.compare)
+
+
 def test_decode_equals_forward_prefix():
     w = random_case(5, 3, 8, 2, 1, 50, 16, dtype="f32")
     q, k, v = w.values("q"), w.values("k"), w.values("v")
