@@ -1,8 +1,10 @@
-"""Build libfa.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+"""Build libfa.so (the HIP kernels and the C ABI) and libfa_ceilings.so (the
+measured-ceiling kernels the benchmark reports beside the attention rows) for
+gfx950, in-tree.
 
 Usage: ``python -m exact_io_aware_16_amd.build`` or ``build()`` from Python.
 Each .hip source is compiled to an object in parallel, then linked into
-``exact_io_aware_16_amd/libfa.so``.
+``exact_io_aware_16_amd/libfa.so`` and ``exact_io_aware_16_amd/libfa_ceilings.so``.
 """
 from __future__ import annotations
 
@@ -15,8 +17,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libfa.so")
+OUT_CEILINGS = os.path.join(PKG, "libfa_ceilings.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
+CEILING_SOURCES = ["fa_ceilings.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,19 +42,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source and link libfa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source and link libfa.so and libfa_ceilings.so;
+    returns the path of libfa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], OUT)
+    _link([objs[s] for s in CEILING_SOURCES], OUT_CEILINGS)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {OUT_CEILINGS}")
     return OUT
 
 

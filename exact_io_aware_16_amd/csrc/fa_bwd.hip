@@ -8,16 +8,17 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D) with D_i = dO_i . O_i,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// MI355X mapping.  Three kernels on one stream, no atomics, so the result is
+// MI355X mapping.  Two kernels on one stream, no atomics, so the result is
 // bitwise reproducible:
-//  1. bwd_delta: D_i = dO_i . O_i in float32 (one row per 16 lanes).
-//  2. bwd_dq (query owner, shaped like the forward pass): each wave owns 32
-//     query rows; S^T = K Q^T and dP^T = V dO^T put one query per lane, so
-//     lse_i and D_i are per-lane scalars; dQ^T += K^T dS^T accumulates in
-//     registers.  K and V blocks stream through a ring of LDS stages filled
-//     by direct-to-LDS loads; K is read both row-wise and with transposing
-//     reads (ds_read_b64_tr_b16) from the same XOR-swizzled tile.
-//  3. bwd_dkdv (key owner): each wave owns 32 keys for the whole pass, K and V
+//  1. bwd_dq (query owner, shaped like the forward pass): each wave owns 32
+//     query rows; it first forms D_i = dO_i . O_i of its rows in float32 (and
+//     writes D and lse_i log2 e for the second kernel); S^T = K Q^T and
+//     dP^T = V dO^T put one query per lane, so lse_i and D_i are per-lane
+//     scalars; dQ^T += K^T dS^T accumulates in registers.  K and V blocks
+//     stream through a ring of LDS stages filled by direct-to-LDS loads; K is
+//     read both row-wise and with transposing reads (ds_read_b64_tr_b16) from
+//     the same XOR-swizzled tile.
+//  2. bwd_dkdv (key owner): each wave owns 32 keys for the whole pass, K and V
 //     rows sit in registers, and for every query head of the group and every
 //     query block S = Q K^T and dP = dO V^T put one key per lane; then
 //     dV^T += dO^T P and dK^T += Q^T dS accumulate in registers.  Q and dO
@@ -29,29 +30,11 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
-// D = rowsum(dO * O) and lse2 computed by the dQ kernel (1) instead of a
-// separate pass over O and dO before it (0)
-#ifndef BWD_FUSE_DELTA
-#define BWD_FUSE_DELTA 1
-#endif
-// gradient tiles staged through LDS and written as whole 128-byte row segments
-// with streaming stores (1), or stored from the accumulator layout (0)
-#ifndef BWD_LDS_EPI
-#define BWD_LDS_EPI 1
-#endif
-
 namespace fa {
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 namespace {
-
-__device__ __forceinline__ void store_grad4(float* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
-}
-__device__ __forceinline__ void store_grad4(uint16_t* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
-}
 
 // Store one wave's 32 x D gradient tile, held in the 32x32 MFMA accumulator
 // layout (lane (n, hf): row n, columns md*32 + 8(i/4) + 4hf + i%4 of acc[md][i]),
@@ -102,39 +85,7 @@ __device__ __forceinline__ void store_tile_rows(G* base, int nrows, const f32x16
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 1. D_i = dO_i . O_i
-// ---------------------------------------------------------------------------
-// Also writes lse2_i = lse_i log2(e) (+inf for rows that saw no key, so that
-// P = exp2(s scale log2 e - lse2) = 0 there), the form the dK/dV kernel streams.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_bf16_kernel(const uint16_t* __restrict__ O,
-                                                             const uint16_t* __restrict__ dO,
-                                                             const float* __restrict__ LSE, float* __restrict__ delta,
-                                                             float* __restrict__ lse2, int rows) {
-    constexpr int LPR = D / 8;  // lanes per row
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    const int row = t / LPR, c8 = t % LPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + c8 * 8);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + c8 * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc = __builtin_fmaf(bf16_bits_to_f32(a[w] & 0xffffu), bf16_bits_to_f32(b[w] & 0xffffu), acc);
-            acc = __builtin_fmaf(bf16_bits_to_f32(a[w] >> 16), bf16_bits_to_f32(b[w] >> 16), acc);
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && c8 == 0) {
-        delta[row] = acc;
-        const float l = LSE[row];
-        lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dQ, query owner
+// 1. dQ, query owner
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTile {
@@ -180,11 +131,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const float lse_v = LSE[qrow];
     // rows with no visible key (lse = -inf) get P = 0
     const float lse2 = lse_v == kNegInf ? __builtin_huge_valf() : lse_v * kLog2e;
-#if BWD_FUSE_DELTA
     // D = dO . O of this query row: O is read in the layout of the dO
     // fragments (this lane's half of the row), the halves meet across lanes
-    // n and n + 32.  The row's D and lse2 go to the workspace for the dK/dV
-    // kernel, which runs after this one.
+    // n and n + 32.  The row's D and lse2 (lse log2 e, +inf for a row that
+    // saw no key so that P = exp2(s scale log2 e - lse2) = 0 there) go to the
+    // workspace for the dK/dV kernel, which runs after this one.
     float dpart = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -197,9 +148,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         delta[qrow] = dlt;
         lse2_out[qrow] = lse2;
     }
-#else
-    const float dlt = delta[qrow];
-#endif
 
     const uint16_t* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
     const uint16_t* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
@@ -300,35 +248,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
-    if constexpr (BWD_LDS_EPI) {
-        static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
-        __syncthreads();   // every wave is past its last ring read: the ring stages the output
-        store_tile_rows<D>(dQ + ((size_t)(b * Hq + h) * Nq + qw) * D, Nq - qw, acc, scale,
-                           reinterpret_cast<uint8_t*>(smem) + wave * 4096, lane);
-        return;
-    }
-    if (qi < Nq) {
-        G* out = dQ + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                store_grad4(out + md * 32 + g * 8 + hf * 4, acc[md][g * 4] * scale, acc[md][g * 4 + 1] * scale,
-                            acc[md][g * 4 + 2] * scale, acc[md][g * 4 + 3] * scale);
-    }
+    static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
+    __syncthreads();   // every wave is past its last ring read: the ring stages the output
+    store_tile_rows<D>(dQ + ((size_t)(b * Hq + h) * Nq + qw) * D, Nq - qw, acc, scale,
+                       reinterpret_cast<uint8_t*>(smem) + wave * 4096, lane);
 }
 
 // ---------------------------------------------------------------------------
-// 3. dK, dV, key owner
+// 2. dK, dV, key owner
 // ---------------------------------------------------------------------------
-// dK/dV loop software-pipelined over query steps (1) or step by step (0);
-// DKV_ILV > 0 interleaves that many vector instructions after each MFMA
-#ifndef DKV_PIPE
-#define DKV_PIPE 1
-#endif
-#ifndef DKV_ILV
-#define DKV_ILV 4
-#endif
+// vector instructions placed after each MFMA of the next step in the
+// software-pipelined dK/dV loop (d = 128)
+constexpr int kDkvInterleave = 4;
 
 template <int D>
 struct DkvTile {
@@ -512,7 +443,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
     };
     // d = 128 only: at d = 64 the second S/dP buffer would halve the waves per SIMD
-    constexpr bool kPipe = DKV_PIPE && D >= 128;
+    constexpr bool kPipe = D >= 128;
     if constexpr (kPipe) {
     // Software-pipelined over steps: iteration stp forms P and dS of step stp
     // and, in the same basic block, issues the S and dP products of step
@@ -602,17 +533,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                     dp[i] = p * (dp[i] - d4[r]);
                 }
             }
-            if (DKV_ILV) {
-                // interleave: the next step's fragment reads, then each of its
-                // MFMAs followed by a few of this step's vector instructions
+            // interleave: the next step's fragment reads, then each of its
+            // MFMAs followed by a few of this step's vector instructions
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            for (int h = 0; h < 2; ++h) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, DKV_ILV, 0);
-                    }
+                for (int m = 0; m < 8; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kDkvInterleave, 0);
                 }
             }
         };
@@ -647,27 +576,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     // the trailing look-ahead loads must land before the workgroup exits
     wait_vmcnt<0>();
-    if constexpr (BWD_LDS_EPI) {
-        static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
-        __syncthreads();   // every wave is past its last ring read: the ring stages the output
-        const size_t o = ((size_t)(b * Hkv + hk) * Nk + kw) * D;
-        uint8_t* stage = reinterpret_cast<uint8_t*>(smem) + wave * 4096;
-        store_tile_rows<D>(dK + o, Nk - kw, dk, scale, stage, lane);
-        store_tile_rows<D>(dV + o, Nk - kw, dv, 1.f, stage, lane);
-        return;
-    }
-    if (kj < Nk) {
-        const size_t o = ((size_t)(b * Hkv + hk) * Nk + kj) * D;
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int dcol = md * 32 + gg * 8 + hf * 4;
-                store_grad4(dK + o + dcol, dk[md][gg * 4] * scale, dk[md][gg * 4 + 1] * scale,
-                            dk[md][gg * 4 + 2] * scale, dk[md][gg * 4 + 3] * scale);
-                store_grad4(dV + o + dcol, dv[md][gg * 4], dv[md][gg * 4 + 1], dv[md][gg * 4 + 2], dv[md][gg * 4 + 3]);
-            }
-    }
+    static_assert(4 * 4096 <= T::LDS_BYTES, "staging needs 4 KB per wave");
+    __syncthreads();   // every wave is past its last ring read: the ring stages the output
+    const size_t o = ((size_t)(b * Hkv + hk) * Nk + kw) * D;
+    uint8_t* stage = reinterpret_cast<uint8_t*>(smem) + wave * 4096;
+    store_tile_rows<D>(dK + o, Nk - kw, dk, scale, stage, lane);
+    store_tile_rows<D>(dV + o, Nk - kw, dv, 1.f, stage, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -839,11 +753,6 @@ static hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
     const int rows = a.B * a.Hq * a.Nq;
     float* lse2 = a.delta + rows;
     hipError_t e;
-    if (!BWD_FUSE_DELTA) {
-        hipLaunchKernelGGL(bwd_delta_bf16_kernel<D>, dim3((rows * (D / 8) + 255) / 256), dim3(256), 0, s,
-                           (const uint16_t*)a.o, (const uint16_t*)a.dO, a.lse, a.delta, lse2, rows);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const float sl2 = a.scale * kLog2e;
     {
         using T = DqTile<D>;

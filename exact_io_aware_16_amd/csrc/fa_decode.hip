@@ -119,14 +119,12 @@ __device__ __forceinline__ void wait_stages(int r) {
 // Share of the stages taken by the wave on the even XCD of each pair, in 64ths
 // (measured on MI355X: waves on odd XCDs stream 10-12% slower; 35/64 was
 // fastest, +2-3% over an even split).
-#ifndef DEC_EVEN64
-#define DEC_EVEN64 35
-#endif
+constexpr int kDecEven64 = 35;
 
 // Start of wave w's range of the S stages (w = G gives S).  Waves go in pairs
 // (2p, 2p+1), which the dispatcher places on an even and an odd XCD (one-wave
 // workgroup w runs on XCD w mod 8); pair p covers [p S / (G/2), (p+1) S / (G/2))
-// and its even wave the first DEC_EVEN64/64 of that.  G is even.
+// and its even wave the first kDecEven64/64 of that.  G is even.
 // (The same integer arithmetic in 32 bits whenever S * (G/2) < 2^31, the usual
 // case: 64-bit divisions are emulated and cost the combine kernel, which
 // evaluates these per piece, far more.)
@@ -137,12 +135,12 @@ __device__ __forceinline__ long long dec_range_start(int w, long long S, int G) 
         const uint32_t s = (uint32_t)S, a = (uint32_t)p * s / (uint32_t)gp;
         if ((w & 1) == 0) return a;
         const uint32_t e = (uint32_t)(p + 1) * s / (uint32_t)gp;
-        return a + (e - a) * DEC_EVEN64 / 64;
+        return a + (e - a) * kDecEven64 / 64;
     }
     const long long a = (long long)p * S / gp;
     if ((w & 1) == 0) return a;
     const long long e = (long long)(p + 1) * S / gp;
-    return a + (e - a) * DEC_EVEN64 / 64;
+    return a + (e - a) * kDecEven64 / 64;
 }
 // the wave whose range holds stage st (0 <= st < S)
 __device__ __forceinline__ int dec_wave_of(long long st, long long S, int G) {
@@ -491,14 +489,12 @@ __global__ __launch_bounds__(D) void decode_stream_combine_kernel(
     if (dcol == 0) LSE[b * Hq + hq] = L > 0.f ? M + log2_fast(L) * kLn2 : kNegInf;
 }
 
-#ifndef DEC_STAGES
-#define DEC_STAGES 2
-#endif
+constexpr int kDecStages = 2;   // ring stages per streaming wave
 
 template <int D, int QR>
 static hipError_t launch_decode_stream(const DecodeArgs& a, int nht) {
-    using T = StreamTile<D, DEC_STAGES, QR>;
-    constexpr auto kern = decode_stream_kernel<D, DEC_STAGES, QR>;
+    using T = StreamTile<D, kDecStages, QR>;
+    constexpr auto kern = decode_stream_kernel<D, kDecStages, QR>;
     hipError_t e = ensure_dynamic_lds<kern>(T::LDS_BYTES);
     if (e != hipSuccess) return e;
     int ncu = 0, lds = 0;

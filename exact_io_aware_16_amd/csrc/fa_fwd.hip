@@ -34,58 +34,17 @@
 
 #include <algorithm>
 
-#ifndef RING_NW64
-#define RING_NW64 4      // waves per workgroup, d = 64
-#endif
-#ifndef RING_S64
-#define RING_S64 2       // ring stages, d = 64
-#endif
-#ifndef RING_NW128
-#define RING_NW128 8     // waves per workgroup, d = 128
-#endif
-#ifndef RING_S128
-#define RING_S128 2      // ring stages, d = 128
-#endif
-#ifndef RING_NT64
-#define RING_NT64 1      // 32-query column tiles per wave, d = 64
-#endif
-#ifndef RING_NT128
-#define RING_NT128 1     // 32-query column tiles per wave, d = 128
-#endif
-// V fragments requested before the exponentials (d = 64, NT = 1)
-#ifndef RING_VH64
-#define RING_VH64 4
-#endif
-// order the S = K Q^T fragment reads ahead of their MFMAs
-#ifndef RING_SGB
-#define RING_SGB 1
-#endif
-// minimum waves per SIMD the d = 64 ring kernel is compiled for (caps its VGPRs)
-// Output tiles staged through LDS and written as whole rows (RING_LDS_EPI),
-// with streaming stores (RING_NT_STORE): complete lines leave for HBM as the
-// workgroups finish instead of waiting, dirty in each XCD's L2, for the
-// write-back at the end of the kernel.  Bit-identical results; +2-3% on the
-// forward shapes measured, +13% on short sequences (B12 H16 N512).  Streaming
-// stores of the accumulator layout itself (8-byte parts of 32 rows per
-// instruction) are 25% slower: every part goes out as a partial line.
-#ifndef RING_LDS_EPI
-#define RING_LDS_EPI 1
-#endif
-#ifndef RING_NT_STORE
-#define RING_NT_STORE 1
-#endif
-#ifndef RING_WPE64
-#define RING_WPE64 2
-#endif
-// softmax row sums on the matrix cores (rowsum_selector) instead of vector adds
-#ifndef RING_LSUM64
-#define RING_LSUM64 1
-#endif
-#ifndef RING_LSUM128
-#define RING_LSUM128 0
-#endif
-
 namespace fa {
+
+// Tile shapes of the bf16 ring kernel (measured on MI355X; see the launchers)
+constexpr int kRingWaves64 = 4;    // waves per workgroup, d = 64
+constexpr int kRingStages64 = 2;   // ring stages, d = 64
+constexpr int kRingWaves128 = 8;   // waves per workgroup, d = 128
+constexpr int kRingStages128 = 2;  // ring stages, d = 128
+// V fragments requested before the exponentials (d = 64, one column tile)
+constexpr int kRingVAhead64 = 4;
+// workgroups per CU the d = 64 ring kernel is compiled for (caps its VGPRs)
+constexpr int kRingWgPerCu64 = 2;
 
 // Lazy rescaling threshold (log2 units): the running max is only raised when
 // some row's block max exceeds it by more than 2^8; until then probabilities
@@ -187,7 +146,8 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
     }
     // row sums on the matrix cores: lacc[nt][0] / [1] of lane j < 16 hold the
     // running sums of queries j and j + 16 of column tile nt
-    constexpr bool kMfmaSum = (D == 64 && RING_LSUM64) || (D == 128 && RING_LSUM128);
+    // (d = 64 only: no gain measured at d = 128)
+    constexpr bool kMfmaSum = D == 64;
     f32x4 lacc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -229,7 +189,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(kf[kk], qf[nt][kk], s[mt][nt]);
             }
-            if (RING_SGB) {
+            {
                 // keep each half's fragment reads together, the second half's
                 // issued while the first half's MFMAs run (left alone, the
                 // compiler serialises every read with its MFMA to save registers)
@@ -290,7 +250,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
             }
             // V fragments of the first key groups are requested before the
             // exponentials so their latency hides behind the vector work.
-            constexpr int VH = (D * NT == 64) ? RING_VH64 : 1;
+            constexpr int VH = (D * NT == 64) ? kRingVAhead64 : 1;
             bf16x8 vf[VH][D / 32];
 #pragma unroll
             for (int ks = 0; ks < VH; ++ks)
@@ -340,12 +300,10 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
     }
     // drain the ring's trailing loads before the workgroup's LDS is reused
     wait_vmcnt<0>();
-    if constexpr (RING_LDS_EPI) {
-        // every wave is past its last ring read and its loads have landed:
-        // the ring becomes the staging area of the output tiles
-        static_assert(NW * NT * 32 * D * 2 <= T::LDS_BYTES, "output tiles must fit in the ring");
-        __syncthreads();
-    }
+    // every wave is past its last ring read and its loads have landed: the
+    // ring becomes the staging area of the output tiles
+    static_assert(NW * NT * 32 * D * 2 <= T::LDS_BYTES, "output tiles must fit in the ring");
+    __syncthreads();
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -360,7 +318,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
             l_tot = pair_sum(l_run[nt]);
         }
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if constexpr (RING_LDS_EPI) {
+        {
             // O rows through LDS: the accumulator layout gives each lane 8-byte
             // pieces of 32 different rows, so stored directly every row is
             // written in sixteen 8-byte parts by eight instructions.  Staged
@@ -387,39 +345,20 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                 const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * D + ((c ^ (r & (CPR - 1))) << 3));
                 const int qr = qw + nt * 32 + r;
                 if (qr < Nq) {
-                    u32x4* dst = reinterpret_cast<u32x4*>(O + ((size_t)(b * Hq + h) * Nq + qr) * D + c * 8);
-                    if constexpr (RING_NT_STORE) __builtin_nontemporal_store(val, dst);
-                    else *dst = val;
+                    __builtin_nontemporal_store(
+                        val, reinterpret_cast<u32x4*>(O + ((size_t)(b * Hq + h) * Nq + qr) * D + c * 8));
                 }
             }
             if (qi < Nq && hf == 0) {
                 const float lv = l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
-                float* dl = LSE + (size_t)(b * Hq + h) * Nq + qi;
-                if constexpr (RING_NT_STORE) __builtin_nontemporal_store(lv, dl);
-                else *dl = lv;
+                __builtin_nontemporal_store(lv, LSE + (size_t)(b * Hq + h) * Nq + qi);
             }
-            continue;
-        }
-        if (qi < Nq) {
-            uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-            for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dcol = md * 32 + g * 8 + hf * 4;
-                    const uint32_t lo = pack_bf16x2(ot[nt][md][g * 4 + 0] * inv, ot[nt][md][g * 4 + 1] * inv);
-                    const uint32_t hi = pack_bf16x2(ot[nt][md][g * 4 + 2] * inv, ot[nt][md][g * 4 + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-                }
-            if (hf == 0)
-                LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                    l_tot > 0.f ? (m_run[nt] + log2_fast(l_tot)) * kLn2 : kNegInf;
         }
     }
 }
 
 template <int D, int NW, int S, int NT, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, ((NW == 4 && D * NT <= 128) ? RING_WPE64 : 1)) void fwd_ring_kernel(
+__global__ __launch_bounds__(NW * 64, ((NW == 4 && D * NT <= 128) ? kRingWgPerCu64 : 1)) void fwd_ring_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, int nqb, int BH,
     float sl2) {
@@ -550,7 +489,7 @@ static hipError_t launch_fwd_ring_t(const FwdArgs& a) {
 static bool fwd64_two_tiles(const FwdArgs& a) {
     int ncu = 256, lds = 0;
     if (device_caps(&ncu, &lds) != hipSuccess) ncu = 256;
-    using T2 = RingTile<64, RING_NW64, RING_S64, 2>;
+    using T2 = RingTile<64, kRingWaves64, kRingStages64, 2>;
     const long long wgs = (long long)((a.Nq + T2::BM - 1) / T2::BM) * a.B * a.Hq;
     return wgs >= (long long)(a.causal ? 4 : 2) * ncu;
 }
@@ -558,13 +497,13 @@ static bool fwd64_two_tiles(const FwdArgs& a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
     if (a.d == 64) {
         if (fwd64_two_tiles(a))
-            return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, 2, true>(a)
-                            : launch_fwd_ring_t<64, RING_NW64, RING_S64, 2, false>(a);
-        return a.causal ? launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, true>(a)
-                        : launch_fwd_ring_t<64, RING_NW64, RING_S64, RING_NT64, false>(a);
+            return a.causal ? launch_fwd_ring_t<64, kRingWaves64, kRingStages64, 2, true>(a)
+                            : launch_fwd_ring_t<64, kRingWaves64, kRingStages64, 2, false>(a);
+        return a.causal ? launch_fwd_ring_t<64, kRingWaves64, kRingStages64, 1, true>(a)
+                        : launch_fwd_ring_t<64, kRingWaves64, kRingStages64, 1, false>(a);
     }
-    return a.causal ? launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, true>(a)
-                    : launch_fwd_ring_t<128, RING_NW128, RING_S128, RING_NT128, false>(a);
+    return a.causal ? launch_fwd_ring_t<128, kRingWaves128, kRingStages128, 1, true>(a)
+                    : launch_fwd_ring_t<128, kRingWaves128, kRingStages128, 1, false>(a);
 }
 
 template <int D>

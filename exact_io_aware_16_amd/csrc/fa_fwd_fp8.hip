@@ -27,25 +27,11 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
-// output rows staged through LDS and written whole with streaming stores (as the bf16 forward)
-#ifndef FP8_LDS_EPI
-#define FP8_LDS_EPI 1
-#endif
-#ifndef FP8_NW128
-#define FP8_NW128 4      // waves per workgroup, d = 128
-#endif
-#ifndef FP8_S128
-#define FP8_S128 3       // ring stages, d = 128
-#endif
-#ifndef FP8_NW64
-#define FP8_NW64 4       // waves per workgroup, d = 64
-#endif
-#ifndef FP8_S64
-#define FP8_S64 3        // ring stages, d = 64
-#endif
-
 namespace fa {
 namespace {
+
+constexpr int kFp8Waves = 4;    // waves per workgroup (d = 64 and 128)
+constexpr int kFp8Stages = 3;   // ring stages (d = 64 and 128)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -257,7 +243,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
     const int qi = qw + n;
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? descale_v / l_tot : 0.f;
-    if constexpr (FP8_LDS_EPI) {
+    {
         // O rows staged through this wave's part of the idle ring and written
         // whole with streaming stores (16 bytes per lane, complete rows per
         // instruction), as in the bf16 forward
@@ -287,22 +273,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
         if (qi < Nq && hf == 0)
             __builtin_nontemporal_store(l_tot > 0.f ? (m_run + log2_fast(l_tot) - kPScaleLog2) * kLn2 : kNegInf,
                                         LSE + (size_t)(b * Hq + h) * Nq + qi);
-        return;
-    }
-    if (qi < Nq) {
-        uint16_t* orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dcol = md * 32 + g * 8 + hf * 4;
-                const uint32_t lo = pack_bf16x2(ot[md][g * 4 + 0] * inv, ot[md][g * 4 + 1] * inv);
-                const uint32_t hi = pack_bf16x2(ot[md][g * 4 + 2] * inv, ot[md][g * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + dcol) = u32x2{lo, hi};
-            }
-        if (hf == 0)
-            LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                l_tot > 0.f ? (m_run + log2_fast(l_tot) - kPScaleLog2) * kLn2 : kNegInf;
     }
 }
 
@@ -324,9 +294,10 @@ hipError_t launch_fp8_t(const Fp8Args& a) {
 
 hipError_t launch_fwd_fp8(const Fp8Args& a) {
     if (a.d == 64)
-        return a.causal ? launch_fp8_t<64, FP8_NW64, FP8_S64, true>(a) : launch_fp8_t<64, FP8_NW64, FP8_S64, false>(a);
-    return a.causal ? launch_fp8_t<128, FP8_NW128, FP8_S128, true>(a)
-                    : launch_fp8_t<128, FP8_NW128, FP8_S128, false>(a);
+        return a.causal ? launch_fp8_t<64, kFp8Waves, kFp8Stages, true>(a)
+                        : launch_fp8_t<64, kFp8Waves, kFp8Stages, false>(a);
+    return a.causal ? launch_fp8_t<128, kFp8Waves, kFp8Stages, true>(a)
+                    : launch_fp8_t<128, kFp8Waves, kFp8Stages, false>(a);
 }
 
 }  // namespace fa

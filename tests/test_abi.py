@@ -10,10 +10,11 @@ import exact_io_aware_16_amd as fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+CEIL_HEADER = os.path.join(ROOT, "include", "fa_ceilings.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(fa_\w+)\s*\(", text, flags=re.M)))
 
@@ -36,6 +37,30 @@ def test_header_declares_the_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_every_header_is_covered():
+    """Each header under include/ belongs to a library the tests load."""
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == ["fa.h",
+                                                                                             "fa_ceilings.h"]
+
+
+def test_ceilings_library_exports_its_header():
+    from exact_io_aware_16_amd import ceilings
+    if not os.path.exists(ceilings.LIB_PATH):
+        pytest.skip("libfa_ceilings.so not built")
+    clib = ceilings.load_library()
+    names = declared_functions(CEIL_HEADER)
+    assert names == ["fa_ceil_device", "fa_ceil_hbm_read", "fa_ceil_lds_read", "fa_ceil_mfma_bf16"], names
+    for n in names:
+        assert hasattr(clib, n), f"{n} not exported"
+    # argument checks happen before anything is launched
+    P = ctypes.c_void_p(0x1000)
+    assert clib.fa_ceil_mfma_bf16(None, P, 1, 1, None) == 1
+    assert clib.fa_ceil_mfma_bf16(P, P, 0, 1, None) == 1
+    assert clib.fa_ceil_hbm_read(P, 17, P, 1, 8, None) == 1      # not a multiple of 16
+    assert clib.fa_ceil_hbm_read(P, 4096, P, 1, 5, None) == 1    # loads in flight not 4/8/16
+    assert clib.fa_ceil_lds_read(P, P, 3, 1, 1, None) == 1       # unknown mode
 
 
 def test_version_and_status_strings(lib):

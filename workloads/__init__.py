@@ -9,7 +9,8 @@ Every stream is ``numpy.random.Generator(PCG64(SeedSequence([42, cfg, t])))``
 with base seed 42 (the seed the pages' own examples use), ``cfg`` the workload
 id and ``t`` the tensor stream:
 
-    0 Q, 1 K, 2 V, 3 dO, 4 outlier key rows, 5 sampled query rows, 6 lengths.
+    0 Q, 1 K, 2 V, 3 dO, 4 outlier key rows, 5 sampled query rows, 6 lengths,
+    7 further query rows for timing the CPU oracle.
 
 Values are ``standard_normal(float32)`` rounded to bfloat16 with
 round-to-nearest-even, so the GPU path and the oracle read the same bits.
@@ -39,7 +40,7 @@ import numpy as np
 BASE_SEED = 42
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = 0, 1, 2, 3
-STREAM_OUTLIER, STREAM_ROWS, STREAM_LENS = 4, 5, 6
+STREAM_OUTLIER, STREAM_ROWS, STREAM_LENS, STREAM_MORE_ROWS = 4, 5, 6, 7
 
 
 def rng(cfg: int, stream: int) -> np.random.Generator:
@@ -213,6 +214,15 @@ def sampled_query_rows(cfg: int, B: int, H: int, N: int, count: int = 512) -> np
     h = (flat // N) % H
     i = flat % N
     return np.stack([b, h, i], axis=1).astype(np.int64)
+
+
+def more_query_rows(cfg: int, B: int, H: int, N: int, count: int) -> np.ndarray:
+    """Further (b, h, i) triples, uniform over all query rows (with repeats
+    possible), from their own stream: the rows the CPU oracle is timed on
+    beyond the parity sample."""
+    g = rng(cfg, STREAM_MORE_ROWS)
+    flat = g.integers(0, B * H * N, size=count, dtype=np.int64)
+    return np.stack([flat // (H * N), (flat // N) % H, flat % N], axis=1).astype(np.int64)
 
 
 def cache_lengths(cfg: int, B: int, lo: int, hi: int) -> np.ndarray:
