@@ -280,7 +280,7 @@ def ceilings():
     hbm = max((C.hbm_read(loads_in_flight=u, wgs_per_cu=g) for u in (4, 8, 16) for g in (4, 8)),
               key=lambda r: r["bytes_per_s"])
     clk = m1["clock_hz"]
-    lds = {m: C.lds_read(m, clk) for m in (0, 1, 2)}
+    lds = {m: C.lds_read(m, clk) for m in (0, 1, 2, 3)}
     return {
         "compute_units": ncu, "peak_core_clock_ghz": peak_clk / 1e9,
         "mfma_bf16_tflops": max(m1["flops_per_s"], m2["flops_per_s"]) / 1e12,
@@ -294,6 +294,7 @@ def ceilings():
         "lds_read_b128_bytes_per_clk_per_cu": lds[0]["bytes_per_clk_per_cu"],
         "lds_read_tr_b16_bytes_per_clk_per_cu": lds[1]["bytes_per_clk_per_cu"],
         "lds_read_b64_bytes_per_clk_per_cu": lds[2]["bytes_per_clk_per_cu"],
+        "lds_read_tr_b16_unswizzled_bytes_per_clk_per_cu": lds[3]["bytes_per_clk_per_cu"],
         "note": "fa_ceilings kernels: 4 independent v_mfma_f32_32x32x16_bf16 chains per wave on every SIMD "
                 "(1 and 2 waves per SIMD); a 4 GiB non-temporal streaming read (best of 4/8/16 loads in flight per "
                 "lane and 4/8 workgroups per CU); 64 KB of LDS re-read by 8 waves per CU (rates from launch time "

@@ -65,5 +65,42 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+OUT_HOSTCHECK = os.path.join(PKG, "libfa_hostcheck.so")
+
+
+def build_hostcheck(verbose: bool = False) -> str:
+    """The C ABI layer (fa_api.hip) with a stub launch layer (host_stubs.cpp)
+    that launches nothing, with AddressSanitizer and UndefinedBehaviorSanitizer
+    on the host code: libfa_hostcheck.so, for tests/test_abi.py run as
+    ``FA_TEST_HOSTCHECK=<path> LD_PRELOAD=<asan runtime> pytest tests/test_abi.py``.
+    Returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    objs = []
+    for src in ("fa_api.hip", "host_stubs.cpp"):
+        obj = os.path.join(BUILD, "hostcheck_" + os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [HIPCC, *FLAGS, *san, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        objs.append(obj)
+    tmp = OUT_HOSTCHECK + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fsanitize=address", "-fsanitize=undefined",
+           "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of libfa_hostcheck.so failed:\n{r.stderr}")
+    os.replace(tmp, OUT_HOSTCHECK)
+    if verbose:
+        print(f"built {OUT_HOSTCHECK}")
+    return OUT_HOSTCHECK
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+    if "--hostcheck" in sys.argv:
+        build_hostcheck(verbose=True)
+    else:
+        build(verbose=True)

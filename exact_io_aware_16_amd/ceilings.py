@@ -118,7 +118,8 @@ def hbm_read(nbytes=4 << 30, wgs_per_cu=8, loads_in_flight=8, reps=10):
 
 def lds_read(mode, clock_hz, wgs_per_cu=2, iters=4000, reps=3):
     """LDS read rate with 4 * wgs_per_cu waves on every CU: mode 0
-    ds_read_b128, mode 1 ds_read_b64_tr_b16, mode 2 ds_read_b64.  Bytes per
+    ds_read_b128, mode 1 ds_read_b64_tr_b16 (swizzled tile), mode 2
+    ds_read_b64, mode 3 ds_read_b64_tr_b16 (unswizzled tile).  Bytes per
     second from the launch time (HIP events), and per core cycle per CU at
     clock_hz (the clock measured under matrix-core load)."""
     import numpy as np

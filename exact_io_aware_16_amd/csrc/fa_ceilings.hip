@@ -98,10 +98,14 @@ __global__ __launch_bounds__(256) void ceil_lds_kernel(uint32_t* __restrict__ si
     __syncthreads();
     const unsigned long long c0 = core_cycles(), w0 = wall_ticks();
     u32x4 acc = {0u, 0u, 0u, 0u};
+    // The read address passes through an empty asm statement every step, so
+    // the compiler cannot see that a window repeats and merge or drop reads
+    // (the data is folded with xor, where equal words would cancel).
     if (mode == 0) {
         for (int it = 0; it < iters; ++it) {
             // 4 KB of consecutive slots per step, a different window every step
-            const int base = ((it * 4 + wave) * 4096) & (kLdsBytes - 1);
+            int base = ((it * 4 + wave) * 4096) & (kLdsBytes - 1);
+            asm volatile("" : "+v"(base));
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 acc ^= *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(lds) +
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(256) void ceil_lds_kernel(uint32_t* __restrict__ si
     } else if (mode == 2) {
         for (int it = 0; it < iters; ++it) {
             // 2 KB of consecutive 8-byte slots per step
-            const int base = ((it * 4 + wave) * 2048) & (kLdsBytes - 1);
+            int base = ((it * 4 + wave) * 2048) & (kLdsBytes - 1);
+            asm volatile("" : "+v"(base));
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(lds) +
@@ -120,19 +125,23 @@ __global__ __launch_bounds__(256) void ceil_lds_kernel(uint32_t* __restrict__ si
             }
         }
     } else {
+        // mode 1: the kernels' swizzled tile; mode 3: the same reads of an
+        // unswizzled tile (chunk c of row r at slot c)
         const int t = lane & 15;
         for (int it = 0; it < iters; ++it) {
-            // a 32-row x 128-column bf16 tile (8 KB, rows of 256 B, chunks
-            // swizzled as in the kernels) per step; the four reads are the two
-            // halves of the fragments at (k0, c0) = (0, 0) and (16, 32)
-            const int tile = ((it * 4 + wave) * 4096) & (kLdsBytes / 2 - 1);
+            // a 32-row x 128-column bf16 tile (8 KB, rows of 256 B) per step;
+            // the four reads are the two halves of the fragments at
+            // (k0, c0) = (0, 0) and (16, 32)
+            int tile = ((it * 4 + wave) * 4096) & (kLdsBytes / 2 - 1);
+            asm volatile("" : "+v"(tile));
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int k0 = (u >> 1) * 16, c0 = (u >> 1) * 32;
                 const int r = k0 + (lane >> 5) * 4 + (t >> 2) + 8 * (u & 1);
                 const int c = c0 + ((lane >> 4) & 1) * 16 + (t & 3) * 4;
+                const int e = mode == 1 ? swz_off<128>(r, c >> 3) + (c & 7) : r * 128 + c;
                 const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4*)(lds + tile + swz_off<128>(r, c >> 3) + (c & 7)));
+                    (__attribute__((address_space(3))) bf16x4*)(lds + tile + e));
                 const u32x2 w = __builtin_bit_cast(u32x2, v);
                 acc[0] ^= w[0];
                 acc[1] ^= w[1];
@@ -193,7 +202,7 @@ int fa_ceil_hbm_read(const void* buf, size_t bytes, void* sink, int workgroups, 
 }
 
 int fa_ceil_lds_read(void* sink, unsigned long long* stamps, int mode, int workgroups, int iters, void* stream) {
-    if (!sink || !stamps || mode < 0 || mode > 2 || workgroups < 1 || iters < 1)
+    if (!sink || !stamps || mode < 0 || mode > 3 || workgroups < 1 || iters < 1)
         return (int)hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fa::ceil_lds_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, fa::kLdsBytes);

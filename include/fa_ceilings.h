@@ -50,7 +50,8 @@ int fa_ceil_hbm_read(const void* buf, size_t bytes, void* sink, int workgroups, 
  * (1 KB per read, conflict-free consecutive slots), mode 1 ds_read_b64_tr_b16
  * (512 B per read, the attention kernels' transposed-fragment addressing of a
  * swizzled 256-byte-row tile), mode 2 ds_read_b64 (512 B per read,
- * consecutive slots).  sink: uint32[256 * workgroups] (written only
+ * consecutive slots), mode 3 ds_read_b64_tr_b16 of the same tile without the
+ * swizzle.  sink: uint32[256 * workgroups] (written only
  * for one data pattern that does not occur).  stamps as fa_ceil_mfma_bf16, per
  * wave, around the read loop. */
 int fa_ceil_lds_read(void* sink, unsigned long long* stamps, int mode, int workgroups, int iters, void* stream);

@@ -19,11 +19,33 @@ def declared_functions(header=HEADER):
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(fa_\w+)\s*\(", text, flags=re.M)))
 
 
+# FA_TEST_HOSTCHECK=<path of libfa_hostcheck.so>: run these checks against the
+# C ABI layer built with AddressSanitizer/UndefinedBehaviorSanitizer over a
+# stub launch layer (exact_io_aware_16_amd.build.build_hostcheck), with the
+# sanitizer runtime preloaded; the success-path tests below then also run.
+HOSTCHECK = os.environ.get("FA_TEST_HOSTCHECK")
+
+
 @pytest.fixture(scope="module")
 def lib():
+    if HOSTCHECK:
+        fa.load_library()   # torch's HIP runtime first, as the binding arranges
+        h = ctypes.CDLL(HOSTCHECK)
+        _declare(h)
+        return h
     if not os.path.exists(fa.LIB_PATH):
         pytest.skip("libfa.so not built")
     return fa.load_library()
+
+
+def _declare(h):
+    """The argument types of every entry point, as the binding declares them."""
+    ref = fa.load_library()
+    for n in declared_functions():
+        fn_ref, fn = getattr(ref, n), getattr(h, n)
+        fn.restype, fn.argtypes = fn_ref.restype, fn_ref.argtypes
+    h.fa_hostcheck_last_launch.restype = ctypes.c_char_p
+    h.fa_hostcheck_last_launch.argtypes = [ctypes.POINTER(ctypes.c_longlong)]
 
 
 def test_header_declares_the_entry_points():
@@ -60,7 +82,7 @@ def test_ceilings_library_exports_its_header():
     assert clib.fa_ceil_mfma_bf16(P, P, 0, 1, None) == 1
     assert clib.fa_ceil_hbm_read(P, 17, P, 1, 8, None) == 1      # not a multiple of 16
     assert clib.fa_ceil_hbm_read(P, 4096, P, 1, 5, None) == 1    # loads in flight not 4/8/16
-    assert clib.fa_ceil_lds_read(P, P, 3, 1, 1, None) == 1       # unknown mode
+    assert clib.fa_ceil_lds_read(P, P, 4, 1, 1, None) == 1       # unknown mode
 
 
 def test_version_and_status_strings(lib):
@@ -290,3 +312,37 @@ def test_binding_rejects_mismatched_tensors(lib):
         fa.prepare_fwd_fp8(q8, k8, k8, o, z(2, 4, dt=f32), 1.0, 1.0, 1.0)
     with pytest.raises(ValueError, match="on the GPU"):
         fa.prepare_fwd_fp8(q8, k8, k8, o, lse, 1.0, 1.0, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# success paths through the stub launch layer (host-check build only): every
+# argument check passes, the workspace layout is computed, and the launch the
+# entry point would make is recorded instead of made
+# ---------------------------------------------------------------------------
+
+def _last(lib):
+    out = (ctypes.c_longlong * 5)()
+    kind = lib.fa_hostcheck_last_launch(out).decode()
+    return kind, list(out)
+
+
+@pytest.mark.skipif(not HOSTCHECK, reason="needs the host-check build (FA_TEST_HOSTCHECK)")
+def test_hostcheck_success_paths(lib):
+    ws, big = P, 1 << 40
+    assert fwd(lib, B=2, Hq=8, Hkv=2, Nq=100, Nk=300, d=128, causal=1) == 0
+    assert _last(lib) == ("fwd_bf16", [2, 8, 100, 128, 1])
+    assert fwd(lib, dtype=0, d=64) == 0 and _last(lib)[0] == "fwd_f32"
+    assert lib.fa_bwd(P, P, P, P, P, P, P, P, P, 1, 1, 4, 2, 64, 64, 128, 1, 0.088, 1, ws, big, N) == 0
+    assert _last(lib) == ("bwd_bf16", [1, 4, 64, 128, 1])
+    assert lib.fa_bwd(P, P, P, P, P, P, P, P, P, 0, 1, 4, 2, 64, 64, 64, 0, 0.125, 0, ws, big, N) == 0
+    assert _last(lib)[0] == "bwd_f32"
+    assert lib.fa_decode(P, P, P, P, P, P, 16, 32, 8, 32768, 128, 1, 0.088, ws, big, N) == 0
+    assert _last(lib) == ("decode", [16, 32, 32768, 128, 1])
+    assert lib.fa_decode(P, P, P, P, P, P, 3, 4, 4, 100, 64, 0, 0.125, ws, big, N) == 0
+    assert _last(lib)[0] == "fwd_f32_lens"
+    assert lib.fa_decode_chunk(P, P, P, P, P, P, 2, 32, 8, 8, 1024, 128, 1, 0.088, 1, ws, big, N) == 0
+    assert _last(lib) == ("decode", [2, 256, 1024, 128, 8])   # Hq * Nq rows, causal chunk of 8
+    assert lib.fa_decode_paged(P, P, P, P, P, P, P, 2, 32, 8, 4, 64, 64, 16, 128, 1, 0.088, 1, ws, big, N) == 0
+    assert _last(lib) == ("decode_paged", [2, 128, 1024, 128, 4])
+    assert lib.fa_fwd_fp8(P, P, P, P, P, 1, 4, 2, 77, 300, 128, 0.5, 0.25, 1.0, 0.088, 1, N) == 0
+    assert _last(lib) == ("fwd_fp8", [1, 4, 77, 128, 1])
