@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp]
+    lib.fa_decode_noalloc.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_paged.restype = i
@@ -282,6 +284,35 @@ def prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, 
 def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=None, stream=None):
     """One query token per head against the first seqlens[b] cached keys."""
     prepare_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, scale=scale, stream=stream)()
+
+
+def prepare_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, scale=None, stream=None):
+    """fa_decode_noalloc's arguments checked and marshalled once (see
+    prepare_fwd): fa_decode without a workspace, its partial results in the
+    library's fixed per-device scratch (calls that overlap on one device race)."""
+    B, Hq, Hkv, one, Nmax, d = _qkv(q, k_cache, v_cache, "k_cache", "v_cache")
+    if one != 1:
+        raise ValueError(f"q must hold one token per head [B, Hq, 1, d], got {tuple(q.shape)}")
+    dcode = _dtype_code(q)
+    _same_dtype(q, ("k_cache", k_cache), ("v_cache", v_cache), ("o", o))
+    _shape(o, q.shape, "o")
+    _f32(lse, "lse")
+    if tuple(lse.shape) not in ((B, Hq), (B, Hq, 1)):
+        raise ValueError(f"lse has shape {tuple(lse.shape)}, expected {(B, Hq)}")
+    _i32(seqlens, "seqlens")
+    _shape(seqlens, (B,), "seqlens")
+    _dev(q, k_cache, v_cache, seqlens, o, lse)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nmax, d,
+            dcode, scale, _stream(stream))
+    return lambda: _check(lib.fa_decode_noalloc(*args))
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, scale=None, stream=None):
+    """fa_decode into caller-provided o and lse without a workspace (the
+    library's fixed device scratch holds the partial results)."""
+    prepare_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, scale=scale, stream=stream)()
 
 
 def prepare_decode_chunk(q, k_cache, v_cache, seqlens, o, lse, workspace, causal=True, scale=None, stream=None):

@@ -4,10 +4,44 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
+// Device scratch of fa_decode_noalloc: one copy per device, reserved when the
+// library's code object is loaded on that device and held until the process
+// ends.  Host code never passes this name to a kernel (on the host it is a
+// stand-in, not a device address); scratch_address() looks up the device
+// address once per device and every launch uses that.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Address of the current device's `scratch`, looked up with
+// hipGetSymbolAddress the first time a device is seen (devices numbered at or
+// past kMaxDevices are looked up on every call).
+hipError_t scratch_address(void** out) {
+    static std::atomic<void*> addr[fa::kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < fa::kMaxDevices;
+    if (cached) {
+        void* p = addr[dev].load(std::memory_order_acquire);
+        if (p) {
+            *out = p;
+            return hipSuccess;
+        }
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    if (cached) addr[dev].store(p, std::memory_order_release);
+    *out = p;
+    return hipSuccess;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -42,6 +76,8 @@ const char* fa_status_str(int status) {
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
         case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
         case FA_ERR_ARG: return "FA_ERR_ARG: scale must be finite and > 0, pointers 16-byte aligned";
+        case FA_ERR_SCRATCH:
+            return "FA_ERR_SCRATCH: the shape needs more device scratch than fa_decode_noalloc's fixed buffer holds";
         default: return "unknown fa status";
     }
 }
@@ -119,6 +155,37 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache, c
                      nullptr, stream};
     float* ws = static_cast<float*>(workspace);
     fa::decode_workspace_layout(a, ws);
+    return from_hip(fa::launch_decode_bf16(a));
+}
+
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                              void* o, float* lse, int B, int Hq, int Hkv, int Nmax, int d, fa_dtype_t dtype,
+                              float scale, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !o || !lse) return FA_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nmax < 1 || d < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (too_big(B, Hq, 1, d) || too_big(B, Hkv, Nmax, d)) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (check_scale(scale) != FA_OK) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(seqlens) || !aligned16(o) ||
+        !aligned4(lse))
+        return FA_ERR_ARG;
+    if (dtype == FA_F32) {
+        // float32 runs the forward kernel with per-sequence key limits: no scratch
+        fa::FwdArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, 1, Nmax, d, scale, 0, stream};
+        return from_hip(fa::launch_fwd_f32(a, seqlens));
+    }
+    // the same partial results as fa_decode, in the fixed scratch instead of a
+    // caller workspace (nothing in it needs to start at zero: each launch
+    // writes every slot its combine reads, and discards the others by select)
+    if (fa::decode_workspace_bytes(B, Hq, Hkv, Nmax, d) > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return FA_ERR_HIP;
+    fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nmax, d, scale, nullptr, nullptr,
+                     nullptr, stream};
+    fa::decode_workspace_layout(a, static_cast<float*>(ws));
     return from_hip(fa::launch_decode_bf16(a));
 }
 

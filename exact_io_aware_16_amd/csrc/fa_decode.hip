@@ -525,21 +525,6 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     return launch_decode_stream<D, 32>(a, nht);
 }
 
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d) {
-    (void)Nmax;
-    const int g = Hq / Hkv, nht = (g + 31) / 32, tr = std::min(g, 32);
-    const size_t slots = (size_t)B * Hkv * nht + kDecodeMaxWaves;
-    return slots * tr * (size_t)(d + 1) * sizeof(float) + ((size_t)B + 1) * sizeof(int);
-}
-
-void decode_workspace_layout(DecodeArgs& a, float* ws) {
-    const int g = a.Hq / a.Hkv, nht = (g + 31) / 32, tr = std::min(g, 32);
-    const size_t rows = ((size_t)a.B * a.Hkv * nht + kDecodeMaxWaves) * tr;
-    a.part_o = ws;
-    a.part_lse = ws + rows * a.d;
-    a.meta = reinterpret_cast<int*>(a.part_lse + rows);
-}
-
 hipError_t launch_decode_bf16(const DecodeArgs& a) {
     return a.d == 64 ? launch_decode_t<64>(a) : launch_decode_t<128>(a);
 }

@@ -147,8 +147,19 @@ hipError_t launch_fwd_fp8(const Fp8Args& a);
 // (B * Hkv * ceil(g / 32) + kDecodeMaxWaves) slots of min(g, 32) rows each,
 // plus B + 1 stage-prefix integers.
 constexpr int kDecodeMaxWaves = 2048;
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d);
+inline size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Nmax, int d) {
+    (void)Nmax;
+    const int g = Hq / Hkv, nht = (g + 31) / 32, tr = g < 32 ? g : 32;
+    const size_t slots = (size_t)B * Hkv * nht + kDecodeMaxWaves;
+    return slots * tr * (size_t)(d + 1) * sizeof(float) + ((size_t)B + 1) * sizeof(int);
+}
 // Points part_o, part_lse and meta of a into the workspace ws.
-void decode_workspace_layout(DecodeArgs& a, float* ws);
+inline void decode_workspace_layout(DecodeArgs& a, float* ws) {
+    const int g = a.Hq / a.Hkv, nht = (g + 31) / 32, tr = g < 32 ? g : 32;
+    const size_t rows = ((size_t)a.B * a.Hkv * nht + kDecodeMaxWaves) * tr;
+    a.part_o = ws;
+    a.part_lse = ws + rows * a.d;
+    a.meta = reinterpret_cast<int*>(a.part_lse + rows);
+}
 
 }  // namespace fa

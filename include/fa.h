@@ -66,7 +66,9 @@ typedef enum {
     FA_ERR_UNSUPPORTED = 4,  /* head dimension d other than 64 or 128           */
     FA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the query says    */
     FA_ERR_HIP = 6,          /* the HIP runtime refused a launch                 */
-    FA_ERR_ARG = 7           /* scale not finite or not > 0                       */
+    FA_ERR_ARG = 7,          /* scale not finite or not > 0                       */
+    FA_ERR_SCRATCH = 8       /* fa_decode_noalloc: the shape needs more scratch   */
+                             /* than its fixed device buffer holds                */
 } fa_status_t;
 
 typedef enum {
@@ -144,6 +146,32 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       int B, int Hq, int Hkv, int Nmax, int d,
                       fa_dtype_t dtype, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of fa_decode_noalloc (per device). */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, results and errors as fa_decode; the
+ * partial results fa_decode keeps in the caller's workspace live instead in a
+ * fixed buffer of FA_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which
+ * the library reserves when its code is loaded on a device and holds until the
+ * process ends.  The call itself allocates nothing and calls no allocating
+ * routine.  Shapes whose fa_decode_workspace_bytes(B, Hq, Hkv, Nmax, d)
+ * exceeds the buffer are refused with FA_ERR_SCRATCH (the decode workload
+ * B16 Hq32 Hkv8 d128 needs 4.3 MiB; at d = 128 the buffer holds B * Hkv up to
+ * 30465 with 4 query heads per K/V head, 14208 with 8, 2016 with 32; at
+ * d = 64 about twice that).
+ * Every call on a device shares that device's buffer, and its contents carry
+ * over from call to call (nothing in it needs to start at zero), so calls
+ * that can overlap on one device (concurrent streams, threads) race and must
+ * be serialised by the caller; calls on different devices are independent.
+ */
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seqlens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nmax, int d,
+                              fa_dtype_t dtype, float scale, void* stream);
 
 /* Bytes of device workspace fa_decode_chunk needs: the same partial results
  * as fa_decode over Hq * Nq query rows.  0 for shapes fa_decode_chunk would

@@ -51,8 +51,9 @@ def _declare(h):
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged",
-              "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes",
-              "fa_decode_paged_workspace_bytes", "fa_abi_version", "fa_status_str"):
+              "fa_decode_noalloc", "fa_bwd_workspace_bytes", "fa_decode_workspace_bytes",
+              "fa_decode_chunk_workspace_bytes", "fa_decode_paged_workspace_bytes", "fa_abi_version",
+              "fa_status_str"):
         assert n in names, names
 
 
@@ -87,10 +88,11 @@ def test_ceilings_library_exports_its_header():
 
 def test_version_and_status_strings(lib):
     assert lib.fa_abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert lib.fa_status_str(s).decode().startswith(["FA_OK", "FA_ERR_NULL_PTR", "FA_ERR_SHAPE",
                                                            "FA_ERR_DTYPE", "FA_ERR_UNSUPPORTED",
-                                                           "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_ARG"][s])
+                                                           "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_ARG",
+                                                           "FA_ERR_SCRATCH"][s])
     assert lib.fa_status_str(99).decode() == "unknown fa status"
 
 
@@ -162,6 +164,23 @@ def test_decode_validation(lib):
     assert dec(wsb=need - 1) == 5
 
 
+def test_decode_noalloc_validation(lib):
+    """Host checks of the no-allocation decode (all refused before any device work)."""
+    def dec(seq=P, B=2, Hq=32, Hkv=8, Nmax=1024, d=128, dtype=1, scale=0.088):
+        return lib.fa_decode_noalloc(P, P, P, seq, P, P, B, Hq, Hkv, Nmax, d, dtype, scale, N)
+    assert dec(seq=N) == 1
+    assert dec(Hq=30) == 2
+    assert dec(Nmax=0) == 2
+    assert dec(dtype=4) == 3
+    assert dec(d=80) == 4
+    assert dec(scale=-1.0) == 7
+    # partial results beyond the fixed 64 MiB scratch: 4 query heads per K/V
+    # head at d = 128 fit up to B * Hkv = 30465
+    assert lib.fa_decode_workspace_bytes(1, 4 * 30466, 30466, 16, 128) > 64 << 20
+    assert dec(B=1, Hq=4 * 30466, Hkv=30466, Nmax=16) == 8
+    assert dec(B=2, Hq=4 * 30466, Hkv=30466, Nmax=16) == 8
+
+
 def test_decode_chunk_validation(lib):
     def chunk(seq=P, ws=P, wsb=1 << 26, d=128, Hq=32, Hkv=8, Nq=8, Nmax=1024, causal=1):
         return lib.fa_decode_chunk(P, P, P, seq, P, P, 2, Hq, Hkv, Nq, Nmax, d, 1, 0.088, causal, ws, wsb, N)
@@ -213,7 +232,7 @@ def test_fwd_fp8_validation(lib):
 
 def test_binding_names_match_header():
     for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_chunk", "fa_decode_paged",
-              "fa_bwd_workspace_bytes",
+              "fa_decode_noalloc", "fa_bwd_workspace_bytes",
               "fa_decode_workspace_bytes", "fa_decode_chunk_workspace_bytes", "fa_decode_paged_workspace_bytes",
               "fa_abi_version"):
         assert callable(getattr(fa, n))
@@ -346,3 +365,6 @@ def test_hostcheck_success_paths(lib):
     assert _last(lib) == ("decode_paged", [2, 128, 1024, 128, 4])
     assert lib.fa_fwd_fp8(P, P, P, P, P, 1, 4, 2, 77, 300, 128, 0.5, 0.25, 1.0, 0.088, 1, N) == 0
     assert _last(lib) == ("fwd_fp8", [1, 4, 77, 128, 1])
+    # the no-allocation decode reaches its scratch lookup, which needs a GPU:
+    # without one it reports FA_ERR_HIP (and launches nothing)
+    assert lib.fa_decode_noalloc(P, P, P, P, P, P, 2, 8, 2, 100, 128, 1, 0.088, N) in (0, 6)
