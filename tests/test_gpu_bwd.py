@@ -159,3 +159,38 @@ def test_backward_beyond_2gib():
         assert_close(f"dV[h={h}]", to_host(dv[0, h]), dV[0, 0], TOL_BF16)
         sel = np.r_[np.random.Generator(np.random.PCG64(h)).integers(0, Nq, 256), np.arange(Nq - 8, Nq)]
         assert_close(f"dQ[h={h}, rows]", to_host(dq[0, h][torch.from_numpy(sel).to(dev)]), dQ[0, 0][sel], TOL_BF16)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_delta_from_stored_o_on_correlated_values(causal):
+    """D_i = dO_i . O_i is formed from the stored (bf16) O, so the kernel's D
+    differs from the exact one by delta_i = dO_i . (O_i - O_exact,i).  That
+    enters the gradients linearly: dQ_i gains -scale delta_i sum_j P_ij k_j
+    and dK_j gains -scale sum_i P_ij delta_i q_i (dV does not use D).  With
+    values that are nearly equal (v_j = vbar + 2^-5 noise), dP_ij - D_i nearly
+    cancels and this term is far above the usual bf16 level; the test checks
+    that the kernel's gradients equal the oracle's plus exactly this term, to
+    the bf16 tolerance, and that without the term they would not."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(77))
+    B, H, N, d = 1, 2, 256, 128
+    w = W.random_case(79, B, H, H, N, N, d, with_do=True)
+    vbar = rng.standard_normal((1, 1, 1, d))
+    v = vbar + 2.0 ** -5 * rng.standard_normal((B, H, N, d))
+    w.tensors["v"] = W.f32_to_bf16_bits(v.astype(np.float32))
+    announce(f"backward, nearly equal values, {'causal' if causal else 'full'}")
+    o, lse, dq, dk, dv = run_fwd_bwd(w, causal)
+    q, k, vv, do = (w.values(n).astype(np.float64) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / np.sqrt(d)
+    O, _ = oracle.ref_fwd(q, k, vv, causal=causal)
+    P = oracle.ref_probs(q, k, causal=causal)
+    dQ, dK, dV = oracle.ref_bwd(q, k, vv, do, causal=causal)
+    delta = (do * (o - O)).sum(-1)                                    # [B, H, N]
+    dQ_pred = dQ - scale * delta[..., None] * (P @ k)
+    dK_pred = dK - scale * np.swapaxes(P, -1, -2) @ (delta[..., None] * q)
+    m_plain = oracle.compare(dq, dQ)
+    print(f"  dQ without the D term: rel_l2={m_plain['rel_l2']:.3e}", flush=True)
+    assert m_plain["rel_l2"] > 5e-3, "inputs do not exercise the D rounding"
+    assert_close("dQ (with the D term)", dq, dQ_pred, TOL_BF16)
+    assert_close("dK (with the D term)", dk, dK_pred, TOL_BF16)
+    assert_close("dV", dv, dV, TOL_BF16)
