@@ -69,6 +69,39 @@ DEC_SOURCES = ["exact_io_aware_16_amd/csrc/fa_decode.hip", "exact_io_aware_16_am
 ROWS = ["fwd_small", "fwd_causal_d64", "fwd_fp8", "fwd_bwd", "fwd_bwd_gqa", "decode", "decode_chunk",
         "decode_paged"]
 
+# Kernels of the three traffic summaries (per call: each launched once).
+HEAD_KERNEL = "fa::fwd_ring_kernel<128, 8, 2, 1, true>"
+BWD_KERNELS = ["fa::bwd_dq_kernel<128, true, float>", "fa::bwd_dkdv_kernel<128, true, float>"]
+DEC_KERNELS = ["fa::decode_stream_kernel<128, 2, 4>", "fa::decode_stream_combine_kernel<128>"]
+
+
+def _pmc_targets():
+    """Per --pmc-target: the bench part to profile, the summary's name, the
+    kernels counted per call, the sources whose digest the summary records,
+    and the algorithmic bytes read and written per call."""
+    # config 3: B2 H32 N8192 d128, causal forward (q, k, v bf16 in; o bf16, lse fp32 out)
+    t3 = 2 * 32 * 8192
+    # config 5: B2 H16 N4096 d128 backward (q, k, v, o, dO bf16 and lse fp32 in; fp32 gradients out)
+    t5 = 2 * 16 * 4096
+    return {
+        "headline": dict(only="headline", name="fwd_bf16_causal_d128_B2H32N8192", kernels=[HEAD_KERNEL],
+                         sources=FWD_SOURCES, read=3 * t3 * 128 * 2, write=t3 * 128 * 2 + t3 * 4,
+                         note="per launch of the causal forward"),
+        "fwd_bwd": dict(only="fwd_bwd", name="bwd_bf16_causal_d128_B2H16N4096", kernels=BWD_KERNELS,
+                        sources=BWD_SOURCES, read=5 * t5 * 128 * 2 + t5 * 4, write=3 * t5 * 128 * 4,
+                        note="per fa_bwd call (dQ kernel + dK/dV kernel); the D and lse log2 e rows the dQ "
+                             "kernel writes for the dK/dV kernel are counted in the measured bytes, not in "
+                             "the algorithmic ones"),
+        "decode": dict(only="decode", name="decode_gqa_B16Hq32Hkv8_N32768_d128", kernels=DEC_KERNELS,
+                       sources=DEC_SOURCES, read=None, write=None,
+                       note="per fa_decode call (stream kernel + combine); the counted launches alternate "
+                            "between the cache states of the bench row; writes include the float32 partial "
+                            "results that the combine kernel reads back"),
+    }
+
+
+PMC_TARGETS = _pmc_targets()
+
 
 def parse_args():
     ap = argparse.ArgumentParser()
@@ -85,8 +118,14 @@ def parse_args():
     ap.add_argument("--only", choices=["headline", "ceilings"] + ROWS, default=None,
                     help="run only this part (for profiling one kernel); prints it as JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run 3 plain 256 MiB device copies (known bytes) to scale rocprofv3 "
+                    help="first run 3 plain 256 MiB device copies (known bytes) to scale rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counts")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="no GPU: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 pass (each run with --calibrate-copy) into profiles/<workload>_traffic.json")
+    ap.add_argument("--pmc-target", choices=sorted(PMC_TARGETS), default="headline",
+                    help="which kernels of the profiled run --pmc-summary reports")
+    ap.add_argument("--pmc-out", default=None, help="where --pmc-summary writes (default profiles/)")
     return ap.parse_args()
 
 
@@ -328,7 +367,7 @@ def headline(args, fa):
     return {
         "w": w, "out": (o, lse), "flops": flops, "avg_s": avg,
         "timing": dict(per_step_us=avg * 1e6, **spread),
-        "roofline": roofline("mfma", flops, avg, "fa::fwd_ring_kernel<128, 8, 2, 1, true>",
+        "roofline": roofline("mfma", flops, avg, HEAD_KERNEL,
                              "fwd_bf16_causal_d128_B2H32N8192", FWD_SOURCES, flops_per_launch=flops,
                              algorithmic_bytes_per_launch=algo_bytes),
     }
@@ -476,8 +515,7 @@ def row_fwd_bwd(args, fa, **override):
            "bwd_flop_convention": "10*B*H*d*pairs (five products, recompute included)",
            "fwd_bwd_tflops": (ff + fb) / (af + ab) / 1e12, "fwd_timing": tf, "bwd_timing": tb,
            "fwd_roofline": roofline("mfma", ff, af, "fa::fwd_ring_kernel<128, 8, 2, 1, true>", flops_per_launch=ff),
-           "bwd_roofline": roofline("mfma", fb, ab, "fa::bwd_dq_kernel<128, true, float> + "
-                                                    "fa::bwd_dkdv_kernel<128, true, float> (one fa_bwd call)",
+           "bwd_roofline": roofline("mfma", fb, ab, " + ".join(BWD_KERNELS) + " (one fa_bwd call)",
                                     "bwd_bf16_causal_d128_B2H16N4096" if not override else None, BWD_SOURCES,
                                     flops_per_launch=fb)}
     if not args.no_parity:
@@ -550,7 +588,7 @@ def row_decode(args, fa):
            "cold_after_writes_gbps": gbps(sd),
            "timing_cold": sc, "warm_per_step_us": aw * 1e6, "timing_cold_after_writes": sd,
            "roofline": roofline("hbm", nbytes, sc["median_us"] * 1e-6,
-                                "fa::decode_stream_kernel<128, 2, 8> + fa::decode_stream_combine_kernel<128>",
+                                " + ".join(DEC_KERNELS),
                                 "decode_gqa_B16Hq32Hkv8_N32768_d128", DEC_SOURCES, algorithmic_bytes_per_launch=nbytes,
                                 timing="median of cache-cold launches"),
            "note": "graded: cold = caches emptied (by reading a 1 GiB buffer) before each launch; "
@@ -632,7 +670,7 @@ def row_decode_paged(args, fa):
            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
            "timing_cold": sc,
            "roofline": roofline("hbm", nbytes, sc["median_us"] * 1e-6,
-                                "fa::decode_stream_kernel<128, 2, 8> (paged) + fa::decode_stream_combine_kernel<128>",
+                                "fa::decode_stream_kernel<128, 2, 4> (paged) + fa::decode_stream_combine_kernel<128>",
                                 algorithmic_bytes_per_launch=nbytes, timing="median of cache-cold launches"),
            "note": "64-key pages at seeded random pool positions; caches emptied (by reading a 1 GiB buffer) "
                    "before each launch"}
@@ -662,9 +700,88 @@ def headline_parity(head):
                   "512 seeded sampled query rows")
 
 
+def _pmc_per_launch(path, counter):
+    """{kernel name: (counter value per launch, launches)} from a rocprofv3
+    counter_collection.csv (rows of one dispatch are summed)."""
+    import csv
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(float))
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return per
+
+
+def pmc_summary(args):
+    """HBM bytes per call of one target's kernels from a FETCH_SIZE and a
+    WRITE_SIZE pass.  Each counter is scaled by what it reads for the three
+    256 MiB calibration copies in the same run (FETCH_SIZE counts about half
+    the bytes a copy reads on this part, WRITE_SIZE all it writes)."""
+    import numpy as np
+    tg = PMC_TARGETS[args.pmc_target]
+    out = {"kernel": " + ".join(tg["kernels"]), "workload": tg["name"],
+           "source_digest": source_digest(tg["sources"])}
+    scale, per_call = {}, {}
+    for counter, path in (("FETCH_SIZE", args.pmc_summary[0]), ("WRITE_SIZE", args.pmc_summary[1])):
+        per = _pmc_per_launch(path, counter)
+        copies = sorted((v for k, d in per.items() if "copyBuffer" in k for v in d.values()), reverse=True)[:3]
+        if len(copies) < 3:
+            raise SystemExit(f"{path}: the three calibration copies are missing (profile with --calibrate-copy)")
+        scale[counter] = (256 << 10) / float(np.mean(copies))   # KiB a 256 MiB copy moves / KiB counted
+        total, launches = 0.0, []
+        for kname in tg["kernels"]:
+            hits = [d for k, d in per.items() if k.startswith("void " + kname + "(") or k.startswith(kname + "(")]
+            if len(hits) != 1:
+                raise SystemExit(f"{path}: kernel {kname} found {len(hits)} times")
+            vals = list(hits[0].values())
+            total += float(np.mean(vals))
+            launches.append(len(vals))
+        per_call[counter] = total
+        out[counter.lower() + "_kib_per_call"] = total
+        out[counter.lower() + "_launches_counted"] = launches
+    rd = per_call["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+    wr = per_call["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+    out["calibration"] = {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 256 MiB, 3 launches)",
+                          "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
+    out.update(hbm_read_bytes_per_call=rd, hbm_write_bytes_per_call=wr, hbm_bytes_per_launch=rd + wr)
+    if tg["read"] is not None:
+        out.update(algorithmic_read_bytes=tg["read"], algorithmic_write_bytes=tg["write"],
+                   read_over_algorithmic=rd / tg["read"], write_over_algorithmic=wr / tg["write"])
+    out["note"] = tg["note"]
+    base = ("cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --pmc {c} -d $R/gpurun_out/pmc_{c}_{t} "
+            "-o run --output-format csv -- python3 $R/bench.py --only {o} --steps 5 --warmup 1 --no-parity --calibrate-copy"
+            "   # R = repository root")
+    out["commands"] = [base.format(c=c, t=args.pmc_target, o=tg["only"]) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+        f"python3 bench.py --pmc-summary <FETCH_SIZE counter_collection.csv> <WRITE_SIZE counter_collection.csv> "
+        f"--pmc-target {args.pmc_target}"]
+    path = args.pmc_out or os.path.join(PROFILES, f"{tg['name']}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def calibrate_copy():
+    """Three plain 256 MiB device-to-device copies: known bytes for scaling
+    the HBM traffic counters of the same profiled run."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     global SETTLE_S
     args = parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     SETTLE_S = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the multi-GPU path is not built. "
@@ -679,6 +796,8 @@ def main():
         sys.exit(1)
     import exact_io_aware_16_amd as fa
     fa.load_library()   # raises if libfa.so is not built: there is no other path
+    if args.calibrate_copy:
+        calibrate_copy()
 
     if args.only in ROW_FUNCS:
         print(json.dumps({args.only: ROW_FUNCS[args.only](args, fa)}), flush=True)
@@ -689,14 +808,6 @@ def main():
 
     log("headline: causal forward B2 H32 N8192 d128 bf16 (1% key rows x8)")
     head = headline(args, fa)
-    if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     if args.only == "headline":
         print(json.dumps({"headline_tflops": head["flops"] / head["avg_s"] / 1e12, "timing": head["timing"]}),
               flush=True)
