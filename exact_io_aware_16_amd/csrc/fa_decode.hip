@@ -28,7 +28,7 @@
 namespace fa {
 
 namespace {
-constexpr float kRescaleThreshold = 8.0f;   // lazy rescaling, as in the forward kernel
+constexpr float kRescaleThreshold = 8.0f;   // lazy rescaling: the max is raised on a jump past 2^8
 }  // namespace
 
 // All V^T fragments of one 32-key stage (frag_tr_swz for k0 = 0, 16 and every

@@ -22,7 +22,7 @@
 //    straight from the row-major V tile by transposing LDS reads, so the
 //    rescale by exp(m_old - m_new) is a per-lane scalar;
 //  * the softmax runs in base 2 with scale*log2(e) folded into one FMA, and the
-//    running max is raised lazily;
+//    running max is raised lazily (only on a jump of 2^64);
 //  * causal: key blocks past the workgroup's last visible key are never
 //    loaded, blocks past a wave's last visible key are skipped by that wave,
 //    and only blocks crossing the diagonal pay for the mask;
@@ -46,11 +46,17 @@ constexpr int kRingVAhead64 = 4;
 // workgroups per CU the d = 64 ring kernel is compiled for (caps its VGPRs)
 constexpr int kRingWgPerCu64 = 2;
 
-// Lazy rescaling threshold (log2 units): the running max is only raised when
-// some row's block max exceeds it by more than 2^8; until then probabilities
-// up to 2^8 are accumulated against the stale max.  O and l share that max, so
-// the final O / l is unchanged (exact up to rounding).
-constexpr float kRescaleThreshold = 8.0f;
+// Lazy rescaling headroom (log2 units): the running max is only raised when
+// some score of a block exceeds it by more than 64, so probabilities up to
+// 2^64 are accumulated against a stale max (fp32 and bf16 hold them; l and O
+// stay far below 2^128).  O and l share that max, so the final O / l is
+// unchanged up to rounding.  Every row sees key 0 in its first block, so the
+// first block sets a finite max and later blocks raise it only on a jump of
+// 2^64, which typical score distributions never reach: the test is one
+// per-lane compare against the lane's own block max, and the exchange between
+// the two lanes of a query row, the rescale and its branch are left to the
+// rare block that fails it.
+constexpr float kRescaleHeadroom = 64.0f;
 
 // ---------------------------------------------------------------------------
 // Ring variant: K/V blocks travel global -> LDS with direct-to-LDS loads
@@ -174,22 +180,45 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
             const uint16_t* sK = smem + st * T::STAGE;
             const uint16_t* sV = sK + T::TILE;
             // ---- S^T = K Q^T ----------------------------------------------------------
-            // K fragments of a 32-key half are requested before its MFMAs, so LDS
-            // latency is paid once per half; each fragment feeds NT MFMAs.
             f32x16 s[2][NT];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                bf16x8 kf[D / 16];
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag_rows_swz<D>(sK, mt * 32, kk * 16, lane);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
+            if constexpr (D == 128 && NT == 1) {
+                // the two 32-key halves' products alternate, so consecutive
+                // MFMAs accumulate into different tiles; fragments are read
+                // eight ahead of the products that use them
+                bf16x8 kf[D / 16][2];
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(kf[kk], qf[nt][kk], s[mt][nt]);
-            }
-            {
+                    for (int mt = 0; mt < 2; ++mt) kf[kk][mt] = frag_rows_swz<D>(sK, mt * 32, kk * 16, lane);
+                s[0][0] = zero16();
+                s[1][0] = zero16();
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) s[mt][0] = mfma32x32x16(kf[kk][mt], qf[0][kk], s[mt][0]);
+                constexpr int NR = 2 * (D / 16), AHEAD = 8;
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, AHEAD, 0);
+#pragma unroll
+                for (int i = 0; i < NR - AHEAD; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, AHEAD, 0);
+            } else {
+                // K fragments of a 32-key half are requested before its MFMAs, so LDS
+                // latency is paid once per half; each fragment feeds NT MFMAs.
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    bf16x8 kf[D / 16];
+#pragma unroll
+                    for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag_rows_swz<D>(sK, mt * 32, kk * 16, lane);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) s[mt][nt] = zero16();
+#pragma unroll
+                    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma32x32x16(kf[kk], qf[nt][kk], s[mt][nt]);
+                }
                 // keep each half's fragment reads together, the second half's
                 // issued while the first half's MFMAs run (left alone, the
                 // compiler serialises every read with its MFMA to save registers)
@@ -215,7 +244,7 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                 }
             }
             // ---- row max, lazy rescale ------------------------------------------------------
-            float mx[NT];
+            float mx[NT];   // this lane's block max (log2 units); lanes n and n + 32 share a row
             bool grow = false;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -225,13 +254,13 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                     m0 = max3f(m0, s[0][nt][i], s[0][nt][i + 1]);
                     m1 = max3f(m1, s[1][nt][i], s[1][nt][i + 1]);
                 }
-                mx[nt] = pair_max(__builtin_fmaxf(m0, m1)) * sl2;
-                grow |= !(mx[nt] <= m_run[nt] + kRescaleThreshold);
+                mx[nt] = __builtin_fmaxf(m0, m1) * sl2;
+                grow |= !(mx[nt] <= m_run[nt] + kRescaleHeadroom);
             }
             if (!wave_all(!grow)) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const float m_new = __builtin_fmaxf(m_run[nt], mx[nt]);
+                    const float m_new = __builtin_fmaxf(m_run[nt], pair_max(mx[nt]));
                     const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m_run[nt] - m_new);
                     if constexpr (kMfmaSum) {
                         const float corr_hi = __int_as_float(
