@@ -72,7 +72,7 @@ ROWS = ["fwd_small", "fwd_causal_d64", "fwd_fp8", "fwd_bwd", "fwd_bwd_gqa", "dec
 # Kernels of the three traffic summaries (per call: each launched once).
 HEAD_KERNEL = "fa::fwd_ring_kernel<128, 8, 2, 1, true>"
 BWD_KERNELS = ["fa::bwd_dq_kernel<128, true, float>", "fa::bwd_dkdv_kernel<128, true, float>"]
-DEC_KERNELS = ["fa::decode_stream_kernel<128, 2, 4>", "fa::decode_stream_combine_kernel<128>"]
+DEC_KERNELS = ["fa::decode_stream_kernel<128, 3, 4>", "fa::decode_stream_combine_kernel<128>"]
 
 
 def _pmc_targets():
@@ -670,7 +670,7 @@ def row_decode_paged(args, fa):
            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
            "timing_cold": sc,
            "roofline": roofline("hbm", nbytes, sc["median_us"] * 1e-6,
-                                "fa::decode_stream_kernel<128, 2, 4> (paged) + fa::decode_stream_combine_kernel<128>",
+                                "fa::decode_stream_kernel<128, 3, 4> (paged) + fa::decode_stream_combine_kernel<128>",
                                 algorithmic_bytes_per_launch=nbytes, timing="median of cache-cold launches"),
            "note": "64-key pages at seeded random pool positions; caches emptied (by reading a 1 GiB buffer) "
                    "before each launch"}
