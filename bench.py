@@ -81,12 +81,18 @@ def _pmc_targets():
     and the algorithmic bytes read and written per call."""
     # config 3: B2 H32 N8192 d128, causal forward (q, k, v bf16 in; o bf16, lse fp32 out)
     t3 = 2 * 32 * 8192
+    # config 2: B4 H16 N2048 d64, causal forward
+    t2 = 4 * 16 * 2048
     # config 5: B2 H16 N4096 d128 backward (q, k, v, o, dO bf16 and lse fp32 in; fp32 gradients out)
     t5 = 2 * 16 * 4096
     return {
         "headline": dict(only="headline", name="fwd_bf16_causal_d128_B2H32N8192", kernels=[HEAD_KERNEL],
                          sources=FWD_SOURCES, read=3 * t3 * 128 * 2, write=t3 * 128 * 2 + t3 * 4,
                          note="per launch of the causal forward"),
+        "fwd_causal_d64": dict(only="fwd_causal_d64", name="fwd_bf16_causal_d64_B4H16N2048",
+                               kernels=["fa::fwd_ring_kernel<64, 4, 2, 1, true>"], sources=FWD_SOURCES,
+                               read=3 * t2 * 64 * 2, write=t2 * 64 * 2 + t2 * 4,
+                               note="per launch of the causal forward"),
         "fwd_bwd": dict(only="fwd_bwd", name="bwd_bf16_causal_d128_B2H16N4096", kernels=BWD_KERNELS,
                         sources=BWD_SOURCES, read=5 * t5 * 128 * 2 + t5 * 4, write=3 * t5 * 128 * 4,
                         note="per fa_bwd call (dQ kernel + dK/dV kernel); the D and lse log2 e rows the dQ "
