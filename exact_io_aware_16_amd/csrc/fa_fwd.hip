@@ -180,12 +180,6 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
             const uint16_t* sK = smem + st * T::STAGE;
             const uint16_t* sV = sK + T::TILE;
             // ---- S^T = K Q^T ----------------------------------------------------------
-            // The wave runs its score products at raised issue priority: of the
-            // two waves on a SIMD, the one with matrix work ready issues first
-            // and the other's vector work fills the cycles the products leave.
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
-            __builtin_amdgcn_sched_barrier(0);
             f32x16 s[2][NT];
             if constexpr (D == 128 && NT == 1) {
                 // the two 32-key halves' products alternate, so consecutive
@@ -234,9 +228,6 @@ __device__ __forceinline__ void fwd_qblock_ring(const uint16_t* __restrict__ Q, 
                 __builtin_amdgcn_sched_group_barrier(kSgDsRead, NKH, 0);
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, NKH * NT * 3 / 2, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
             // ---- mask (diagonal / tail blocks only) ---------------------------------------
             if (key0 + T::BN > mask_from || key0 + T::BN > kv_end) {
 #pragma unroll
