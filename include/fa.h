@@ -39,8 +39,9 @@
  *   pointer after returning.  Its only global state is a per-device cache of
  *   facts looked up on first use (compute-unit count, LDS size, each kernel's
  *   dynamic-LDS attribute), filled idempotently and safe to race on, so calls
- *   on different streams or threads are independent.  Outputs are fully
- *   overwritten.
+ *   on different streams or threads are independent; and the fixed device
+ *   scratch of fa_decode_noalloc (declared below), whose calls on one device
+ *   share it.  Outputs are fully overwritten.
  * - Errors: host-visible arguments are checked before anything is enqueued;
  *   on any error nothing is launched and a status != FA_OK is returned.  A
  *   failed kernel launch returns FA_ERR_HIP.  No exception crosses the ABI.
