@@ -755,9 +755,9 @@ def pmc_summary(args):
         out.update(algorithmic_read_bytes=tg["read"], algorithmic_write_bytes=tg["write"],
                    read_over_algorithmic=rd / tg["read"], write_over_algorithmic=wr / tg["write"])
     out["note"] = tg["note"]
-    base = ("cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --pmc {c} -d $R/gpurun_out/pmc_{c}_{t} "
+    base = ("cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --pmc {c} -d $OUT/pmc_{c}_{t} "
             "-o run --output-format csv -- python3 $R/bench.py --only {o} --steps 5 --warmup 1 --no-parity --calibrate-copy"
-            "   # R = repository root")
+            "   # R = repository root, OUT = any output directory")
     out["commands"] = [base.format(c=c, t=args.pmc_target, o=tg["only"]) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
         f"python3 bench.py --pmc-summary <FETCH_SIZE counter_collection.csv> <WRITE_SIZE counter_collection.csv> "
         f"--pmc-target {args.pmc_target}"]
