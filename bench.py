@@ -324,6 +324,8 @@ def ceilings():
     m2 = C.mfma_bf16(waves_per_simd=2)
     hbm = max((C.hbm_read(loads_in_flight=u, wgs_per_cu=g) for u in (4, 8, 16) for g in (4, 8)),
               key=lambda r: r["bytes_per_s"])
+    hbm_lds = max((C.hbm_read_lds(waves_per_cu=w, stage_kb=16, stages=st, nontemporal=nt)
+                   for nt in (True, False) for st in (2, 3) for w in (3, 4, 8)), key=lambda r: r["bytes_per_s"])
     clk = m1["clock_hz"]
     lds = {m: C.lds_read(m, clk) for m in (0, 1, 2, 3)}
     return {
@@ -336,13 +338,17 @@ def ceilings():
         "hbm_read_gbps": hbm["bytes_per_s"] / 1e9,
         "hbm_read_frac_of_peak": hbm["bytes_per_s"] / PEAK_HBM,
         "hbm_read_config": {"workgroups": hbm["workgroups"], "loads_in_flight": hbm["loads_in_flight"]},
+        "hbm_read_direct_to_lds_gbps": hbm_lds["bytes_per_s"] / 1e9,
+        "hbm_read_direct_to_lds_frac_of_peak": hbm_lds["bytes_per_s"] / PEAK_HBM,
+        "hbm_read_direct_to_lds_config": {k: hbm_lds[k] for k in ("workgroups", "stage_kb", "stages", "nontemporal")},
         "lds_read_b128_bytes_per_clk_per_cu": lds[0]["bytes_per_clk_per_cu"],
         "lds_read_tr_b16_bytes_per_clk_per_cu": lds[1]["bytes_per_clk_per_cu"],
         "lds_read_b64_bytes_per_clk_per_cu": lds[2]["bytes_per_clk_per_cu"],
         "lds_read_tr_b16_unswizzled_bytes_per_clk_per_cu": lds[3]["bytes_per_clk_per_cu"],
         "note": "fa_ceilings kernels: 4 independent v_mfma_f32_32x32x16_bf16 chains per wave on every SIMD "
                 "(1 and 2 waves per SIMD); a 4 GiB non-temporal streaming read (best of 4/8/16 loads in flight per "
-                "lane and 4/8 workgroups per CU); 64 KB of LDS re-read by 8 waves per CU (rates from launch time "
+                "lane and 4/8 workgroups per CU); the same read through direct-to-LDS loads (one-wave workgroups, "
+                "16 KB stages, best of 2/3 stages, 3/4/8 waves per CU, default or non-temporal policy); 64 KB of LDS re-read by 8 waves per CU (rates from launch time "
                 "at the clock measured under MFMA load); clock = core-cycle counter over the constant-rate counter "
                 "during the MFMA loop",
     }

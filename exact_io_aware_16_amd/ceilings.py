@@ -33,6 +33,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_ceil_hbm_read.argtypes = [vp, sz, vp, i, i, vp]
     lib.fa_ceil_lds_read.restype = i
     lib.fa_ceil_lds_read.argtypes = [vp, vp, i, i, i, vp]
+    lib.fa_ceil_hbm_read_lds_bytes.restype = ctypes.c_longlong
+    lib.fa_ceil_hbm_read_lds_bytes.argtypes = [sz, i, i]
+    lib.fa_ceil_hbm_read_lds.restype = i
+    lib.fa_ceil_hbm_read_lds.argtypes = [vp, sz, i, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -114,6 +118,27 @@ def hbm_read(nbytes=4 << 30, wgs_per_cu=8, loads_in_flight=8, reps=10):
     torch.cuda.empty_cache()
     return {"bytes_per_s": nbytes / float(np.median(ts)), "bytes": nbytes, "workgroups": wgs,
             "loads_in_flight": loads_in_flight}
+
+
+def hbm_read_lds(nbytes=4 << 30, waves_per_cu=4, stage_kb=16, stages=3, nontemporal=True, reps=10):
+    """Streaming-read bandwidth (bytes/s) through direct-to-LDS loads, one-wave
+    workgroups with a private ring of `stages` stages of `stage_kb` KB."""
+    import numpy as np
+    import torch
+    lib = load_library()
+    ncu, _, _ = device()
+    wgs = ncu * waves_per_cu
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    nread = lib.fa_ceil_hbm_read_lds_bytes(nbytes, wgs, stage_kb)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    launch = lambda: _ok(lib.fa_ceil_hbm_read_lds(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs, stage_kb, stages,
+                                                  1 if nontemporal else 0, stream), "fa_ceil_hbm_read_lds")
+    launch()
+    ts = _timed(launch, reps)
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes_per_s": nread / float(np.median(ts)), "bytes": nread, "workgroups": wgs, "stage_kb": stage_kb,
+            "stages": stages, "nontemporal": bool(nontemporal)}
 
 
 def lds_read(mode, clock_hz, wgs_per_cu=2, iters=4000, reps=3):

@@ -79,6 +79,28 @@ __global__ __launch_bounds__(256) void ceil_read_kernel(const u32x4* __restrict_
     if (acc[0] == never && acc[1] == never) sink[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Streaming read through direct-to-LDS loads, the form the decode streams
+// its cache with: one-wave workgroups, each reading its contiguous share of
+// the buffer in 1 KB instructions (64 lanes x 16 B) into a ring of NS stages
+// of L instructions, keeping at most NS - 1 stages in flight.  POL is the
+// cache-policy operand (0 default, 2 non-temporal).
+template <int L, int NS, int POL>
+__global__ __launch_bounds__(64) void ceil_read_lds_kernel(const u32x4* __restrict__ buf, long long units_per_wave) {
+    extern __shared__ __align__(16) u32x4 ring[];
+    const int lane = threadIdx.x;
+    const u32x4* src = buf + (long long)blockIdx.x * units_per_wave * 64 + lane;
+    const long long nst = units_per_wave / L;
+    for (long long k = 0; k < nst; ++k) {
+        u32x4* dst = ring + (int)(k % NS) * L * 64;
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            __builtin_amdgcn_global_load_lds(src + (k * L + i) * 64, (__attribute__((address_space(3))) void*)(dst + i * 64),
+                                             16, 0, POL);
+        wait_vmcnt<(NS - 1) * L>();
+    }
+    wait_vmcnt<0>();
+}
+
 // LDS read bandwidth.  Each workgroup fills 64 KB of LDS, then every wave
 // reads it `iters` times over: mode 0 with 16-byte reads (ds_read_b128, 64
 // lanes x 16 B = 1 KB per instruction, consecutive lanes on consecutive 16-byte
@@ -163,6 +185,35 @@ __global__ __launch_bounds__(256) void ceil_lds_kernel(uint32_t* __restrict__ si
 }  // namespace
 }  // namespace fa
 
+namespace fa {
+namespace {
+template <int L, int NS>
+hipError_t launch_read_lds(const u32x4* b, long long upw, int workgroups, int nt, hipStream_t st) {
+    const int lds = L * NS * 1024;
+    if (nt) {
+        constexpr auto kern = ceil_read_lds_kernel<L, NS, 2>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(workgroups), dim3(64), lds, st, b, upw);
+    } else {
+        constexpr auto kern = ceil_read_lds_kernel<L, NS, 0>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(workgroups), dim3(64), lds, st, b, upw);
+    }
+    return hipGetLastError();
+}
+template <int L>
+hipError_t launch_read_lds_l(const u32x4* b, long long upw, int workgroups, int stages, int nt, hipStream_t st) {
+    if (stages == 2) return launch_read_lds<L, 2>(b, upw, workgroups, nt, st);
+    if (stages == 3) return launch_read_lds<L, 3>(b, upw, workgroups, nt, st);
+    return launch_read_lds<L, 4>(b, upw, workgroups, nt, st);
+}
+}  // namespace
+}  // namespace fa
+
 extern "C" {
 
 int fa_ceil_device(int* ncu, int* wall_clock_khz, int* peak_clock_khz) {
@@ -199,6 +250,27 @@ int fa_ceil_hbm_read(const void* buf, size_t bytes, void* sink, int workgroups, 
     else
         hipLaunchKernelGGL(fa::ceil_read_kernel<16>, dim3(workgroups), dim3(256), 0, st, b, n16, k, 0x9E3779B9u);
     return (int)hipGetLastError();
+}
+
+long long fa_ceil_hbm_read_lds_bytes(size_t bytes, int workgroups, int stage_kb) {
+    if (workgroups < 1 || (stage_kb != 4 && stage_kb != 8 && stage_kb != 16)) return 0;
+    const long long upw = (long long)(bytes / 1024) / workgroups / stage_kb * stage_kb;
+    return upw * 1024 * workgroups;
+}
+
+int fa_ceil_hbm_read_lds(const void* buf, size_t bytes, int workgroups, int stage_kb, int stages, int nontemporal,
+                         void* stream) {
+    if (!buf || (reinterpret_cast<uintptr_t>(buf) & 15) || workgroups < 1 ||
+        (stage_kb != 4 && stage_kb != 8 && stage_kb != 16) || stages < 2 || stages > 4 ||
+        (nontemporal != 0 && nontemporal != 1))
+        return (int)hipErrorInvalidValue;
+    const long long upw = (long long)(bytes / 1024) / workgroups / stage_kb * stage_kb;
+    if (upw < stage_kb) return (int)hipErrorInvalidValue;
+    const auto* b = static_cast<const fa::u32x4*>(buf);
+    const hipStream_t st = (hipStream_t)stream;
+    if (stage_kb == 4) return (int)fa::launch_read_lds_l<4>(b, upw, workgroups, stages, nontemporal, st);
+    if (stage_kb == 8) return (int)fa::launch_read_lds_l<8>(b, upw, workgroups, stages, nontemporal, st);
+    return (int)fa::launch_read_lds_l<16>(b, upw, workgroups, stages, nontemporal, st);
 }
 
 int fa_ceil_lds_read(void* sink, unsigned long long* stamps, int mode, int workgroups, int iters, void* stream) {

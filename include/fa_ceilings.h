@@ -45,6 +45,19 @@ int fa_ceil_mfma_bf16(float* sink, unsigned long long* stamps, int workgroups, i
 int fa_ceil_hbm_read(const void* buf, size_t bytes, void* sink, int workgroups, int loads_in_flight,
                      void* stream);
 
+/* Streaming read through direct-to-LDS loads (global_load_lds_dwordx4), the
+ * load form the decode streams its cache with: `workgroups` one-wave
+ * workgroups each read a contiguous share of buf (16-byte aligned) in 1 KB
+ * instructions into a private LDS ring of `stages` (2..4) stages of
+ * `stage_kb` (4, 8 or 16) KB, at most stages - 1 stages in flight, with the
+ * default (nontemporal = 0) or the non-temporal (1) cache policy.  The bytes
+ * read are fa_ceil_hbm_read_lds_bytes(bytes, workgroups, stage_kb) (each share
+ * rounded down to whole stages); that function returns 0 for arguments the
+ * read refuses. */
+long long fa_ceil_hbm_read_lds_bytes(size_t bytes, int workgroups, int stage_kb);
+int fa_ceil_hbm_read_lds(const void* buf, size_t bytes, int workgroups, int stage_kb, int stages, int nontemporal,
+                         void* stream);
+
 /* LDS read rate: each of `workgroups` (256 lanes, 64 KB of LDS each) fills its
  * LDS, then each of its 4 waves reads 4 * iters times: mode 0 ds_read_b128
  * (1 KB per read, conflict-free consecutive slots), mode 1 ds_read_b64_tr_b16

@@ -74,7 +74,8 @@ def test_ceilings_library_exports_its_header():
         pytest.skip("libfa_ceilings.so not built")
     clib = ceilings.load_library()
     names = declared_functions(CEIL_HEADER)
-    assert names == ["fa_ceil_device", "fa_ceil_hbm_read", "fa_ceil_lds_read", "fa_ceil_mfma_bf16"], names
+    assert names == ["fa_ceil_device", "fa_ceil_hbm_read", "fa_ceil_hbm_read_lds", "fa_ceil_hbm_read_lds_bytes",
+                     "fa_ceil_lds_read", "fa_ceil_mfma_bf16"], names
     for n in names:
         assert hasattr(clib, n), f"{n} not exported"
     # argument checks happen before anything is launched
@@ -84,6 +85,15 @@ def test_ceilings_library_exports_its_header():
     assert clib.fa_ceil_hbm_read(P, 17, P, 1, 8, None) == 1      # not a multiple of 16
     assert clib.fa_ceil_hbm_read(P, 4096, P, 1, 5, None) == 1    # loads in flight not 4/8/16
     assert clib.fa_ceil_lds_read(P, P, 4, 1, 1, None) == 1       # unknown mode
+    # direct-to-LDS streaming read: shares rounded down to whole stages
+    assert clib.fa_ceil_hbm_read_lds_bytes(1 << 30, 1024, 16) == (1 << 30)
+    assert clib.fa_ceil_hbm_read_lds_bytes((1 << 20) + 5000, 4, 16) == 4 * 256 * 1024
+    assert clib.fa_ceil_hbm_read_lds_bytes(1 << 20, 4, 12) == 0
+    assert clib.fa_ceil_hbm_read_lds(P, 1 << 20, 4, 12, 2, 1, None) == 1     # stage size not 4/8/16 KB
+    assert clib.fa_ceil_hbm_read_lds(P, 1 << 20, 4, 16, 5, 1, None) == 1     # stages not 2..4
+    assert clib.fa_ceil_hbm_read_lds(P, 1 << 20, 4, 16, 2, 3, None) == 1     # policy not 0/1
+    assert clib.fa_ceil_hbm_read_lds(P, 1 << 14, 4, 16, 2, 1, None) == 1     # less than a stage per wave
+    assert clib.fa_ceil_hbm_read_lds(ctypes.c_void_p(0x1001), 1 << 20, 4, 16, 2, 1, None) == 1   # misaligned
 
 
 def test_version_and_status_strings(lib):
