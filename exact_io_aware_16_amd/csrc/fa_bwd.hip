@@ -151,6 +151,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     const uint16_t* kb = K + (size_t)(b * Hkv + hk) * Nk * D;
     const uint16_t* vb = V + (size_t)(b * Hkv + hk) * Nk * D;
+    // -D of this lane's query row in every element: the dP^T products
+    // accumulate onto it, so dP - D costs no vector instruction per block
+    f32x16 negd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = -dlt;
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, qb * T::BM + T::BM + off);
     const int nblk = (kv_end + T::BN - 1) / T::BN;
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         if (key0 < wave_end) {
             const uint16_t* sK = smem + slot * T::STAGE;
             const uint16_t* sV = sK + T::TILE;
-            f32x16 s = zero16(), dp = zero16();
+            f32x16 s = zero16(), dp = negd;   // the products give dP^T - D directly
 #pragma unroll
             for (int k0 = 0; k0 < D / 16; k0 += 4) {
                 bf16x8 ka[4], va[4];
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                         const bool ok = key < kv_end && (!CAUSAL || key <= qi + off);
                         p = ok ? p : 0.f;
                     }
-                    s[i] = p * (dp[i] - dlt);  // dS^T
+                    s[i] = p * dp[i];  // dS^T = P (dP - D)
                 }
             };
             if (need_mask) form_ds(std::true_type{});
