@@ -73,6 +73,8 @@ ROWS = ["fwd_small", "fwd_causal_d64", "fwd_fp8", "fwd_bwd", "fwd_bwd_gqa", "dec
 HEAD_KERNEL = "fa::fwd_ring_kernel<128, 8, 2, 1, true>"
 BWD_KERNELS = ["fa::bwd_dq_kernel<128, true, float>", "fa::bwd_dkdv_kernel<128, true, float>"]
 DEC_KERNELS = ["fa::decode_stream_kernel<128, 3, 4>", "fa::decode_stream_combine_kernel<128>"]
+CHUNK_KERNELS = ["fa::decode_stream_kernel<128, 2, 32>", "fa::decode_stream_combine_kernel<128>"]
+FP8_KERNEL = "fa::(anonymous namespace)::fwd_fp8_kernel<128, 4, 3, true>"
 
 
 def _pmc_targets():
@@ -98,6 +100,15 @@ def _pmc_targets():
                         note="per fa_bwd call (dQ kernel + dK/dV kernel); the D and lse log2 e rows the dQ "
                              "kernel writes for the dK/dV kernel are counted in the measured bytes, not in "
                              "the algorithmic ones"),
+        "fwd_fp8": dict(only="fwd_fp8", name="fwd_fp8_causal_d128_B2H32N8192", kernels=[FP8_KERNEL],
+                        sources=FP8_SOURCES, read=3 * t3 * 128, write=t3 * 128 * 2 + t3 * 4,
+                        note="per launch of the causal FP8 forward (E4M3 q, k, v in; bf16 o, fp32 lse out)"),
+        "decode_chunk": dict(only="decode_chunk", name="decode_chunk_gqa_B16Hq32Hkv8_Nq8_N32768_d128",
+                             kernels=CHUNK_KERNELS, sources=DEC_SOURCES, read=None, write=None,
+                             note="per fa_decode_chunk call (stream kernel + combine), cache-cold launches"),
+        "decode_paged": dict(only="decode_paged", name="decode_paged_gqa_B16Hq32Hkv8_N32768_d128_page64",
+                             kernels=DEC_KERNELS, sources=DEC_SOURCES, read=None, write=None,
+                             note="per fa_decode_paged call (stream kernel + combine), cache-cold launches"),
         "decode": dict(only="decode", name="decode_gqa_B16Hq32Hkv8_N32768_d128", kernels=DEC_KERNELS,
                        sources=DEC_SOURCES, read=None, write=None,
                        note="per fa_decode call (stream kernel + combine); the counted launches alternate "
@@ -491,7 +502,8 @@ def row_fwd_fp8(args, fa):
     flops = 4.0 * w.B * w.Hq * w.d * causal_pairs(w.Nq, w.Nk)
     out = {"workload": "llama_causal_fwd_B2_H32_N8192_d128_fp8_e4m3_kout", "tflops": flops / avg / 1e12,
            "frac_of_fp8_peak": flops / avg / PEAK_FP8, "timing": tm,
-           "roofline": roofline("mfma", flops, avg, "fa::fwd_fp8_kernel<128, 4, 3, true>", peak=PEAK_FP8,
+           "roofline": roofline("mfma", flops, avg, FP8_KERNEL, "fwd_fp8_causal_d128_B2H32N8192", FP8_SOURCES,
+                                peak=PEAK_FP8,
                                 flops_per_launch=flops, dtype="fp8 e4m3")}
     if not args.no_parity:
         vals = {n: oracle.e4m3_value(c) * s for n, (c, s) in f8.items()}
@@ -639,8 +651,9 @@ def row_decode_chunk(args, fa):
            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
            "tflops": flops / (sc["median_us"] * 1e-6) / 1e12, "timing_cold": sc,
            "roofline": roofline("hbm", nbytes, sc["median_us"] * 1e-6,
-                                "fa::decode_stream_kernel<128, 2, 32> + fa::decode_stream_combine_kernel<128>",
-                                algorithmic_bytes_per_launch=nbytes, timing="median of cache-cold launches"),
+                                " + ".join(CHUNK_KERNELS), "decode_chunk_gqa_B16Hq32Hkv8_Nq8_N32768_d128",
+                                DEC_SOURCES, algorithmic_bytes_per_launch=nbytes,
+                                timing="median of cache-cold launches"),
            "note": "caches emptied (by reading a 1 GiB buffer) before each launch"}
     if not args.no_parity:
         O, L = oracle.ref_decode_chunk(w.values("q"), w.values("k"), w.values("v"), w.seqlens, causal=True,
@@ -682,8 +695,9 @@ def row_decode_paged(args, fa):
            "algorithmic_bytes": nbytes, "cold_gbps": gbps, "cold_frac_of_hbm": gbps * 1e9 / PEAK_HBM,
            "timing_cold": sc,
            "roofline": roofline("hbm", nbytes, sc["median_us"] * 1e-6,
-                                "fa::decode_stream_kernel<128, 3, 4> (paged) + fa::decode_stream_combine_kernel<128>",
-                                algorithmic_bytes_per_launch=nbytes, timing="median of cache-cold launches"),
+                                " + ".join(DEC_KERNELS) + " (paged)", "decode_paged_gqa_B16Hq32Hkv8_N32768_d128_page64",
+                                DEC_SOURCES, algorithmic_bytes_per_launch=nbytes,
+                                timing="median of cache-cold launches"),
            "note": "64-key pages at seeded random pool positions; caches emptied (by reading a 1 GiB buffer) "
                    "before each launch"}
     if not args.no_parity:
