@@ -1,6 +1,8 @@
 // C ABI of libfa (declared in include/fa.h): argument validation, workspace
 // sizing and launch.  Every check happens on the host before anything is
-// enqueued; the library keeps no state between calls.
+// enqueued.  Between calls the library keeps only per-device facts looked up
+// once (CU count, LDS size, each kernel's dynamic-LDS attribute, the address
+// of fa_decode_noalloc's scratch) and that scratch itself.
 #include <math.h>
 #include <stdint.h>
 
