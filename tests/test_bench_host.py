@@ -55,3 +55,27 @@ def test_pmc_summary_refuses_a_run_without_calibration(tmp_path):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", str(tmp_path / "f.csv"),
                         str(tmp_path / "w.csv"), "--pmc-out", str(tmp_path / "t.json")], capture_output=True, text=True)
     assert r.returncode != 0 and "calibration copies" in (r.stderr + r.stdout)
+
+
+def test_committed_traffic_files_describe_their_targets():
+    """Every profiles/<workload>_traffic.json that bench.py reads names the
+    kernels and workload of its --pmc-target, and carries the per-call bytes,
+    the calibration scales and the commands that made it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    seen = 0
+    for target, tg in bench.PMC_TARGETS.items():
+        path = os.path.join(ROOT, "profiles", f"{tg['name']}_traffic.json")
+        if not os.path.exists(path):
+            continue
+        seen += 1
+        with open(path) as f:
+            t = json.load(f)
+        assert t["workload"] == tg["name"], target
+        assert t["kernel"] == " + ".join(tg["kernels"]), target
+        assert t["hbm_bytes_per_launch"] == t["hbm_read_bytes_per_call"] + t["hbm_write_bytes_per_call"], target
+        assert t["hbm_read_bytes_per_call"] > 0 and t["hbm_write_bytes_per_call"] > 0, target
+        assert 1.5 < t["calibration"]["fetch_scale"] < 2.5 and 0.8 < t["calibration"]["write_scale"] < 1.2, target
+        assert any(f"--pmc-target {target}" in c for c in t["commands"]), target
+        assert len(t["source_digest"]) == 16, target
+    assert seen >= 4
