@@ -79,3 +79,12 @@ def test_committed_traffic_files_describe_their_targets():
         assert any(f"--pmc-target {target}" in c for c in t["commands"]), target
         assert len(t["source_digest"]) == 16, target
     assert seen >= 4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus N with N > 1 exits with a message before touching a GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
