@@ -100,6 +100,12 @@ def _pmc_targets():
                         note="per fa_bwd call (dQ kernel + dK/dV kernel); the D and lse log2 e rows the dQ "
                              "kernel writes for the dK/dV kernel are counted in the measured bytes, not in "
                              "the algorithmic ones"),
+        "fwd_bwd_gqa": dict(only="fwd_bwd_gqa", name="bwd_bf16_causal_gqa_d128_B2Hq32Hkv8N4096", kernels=BWD_KERNELS,
+                            sources=BWD_SOURCES, read=3 * 2 * t5 * 128 * 2 + 2 * (t5 // 2) * 128 * 2 + 2 * t5 * 4,
+                            write=2 * t5 * 128 * 4 + 2 * (t5 // 2) * 128 * 4,
+                            note="per fa_bwd call (dQ kernel + dK/dV kernel) at B2 Hq32 Hkv8 N4096: q, o, dO and "
+                                 "lse over 32 query heads, k and v over 8 K/V heads read; dq over 32 heads, dk and "
+                                 "dv over 8 written (fp32)"),
         "fwd_fp8": dict(only="fwd_fp8", name="fwd_fp8_causal_d128_B2H32N8192", kernels=[FP8_KERNEL],
                         sources=FP8_SOURCES, read=3 * t3 * 128, write=t3 * 128 * 2 + t3 * 4,
                         note="per launch of the causal FP8 forward (E4M3 q, k, v in; bf16 o, fp32 lse out)"),
@@ -540,7 +546,8 @@ def row_fwd_bwd(args, fa, **override):
            "fwd_bwd_tflops": (ff + fb) / (af + ab) / 1e12, "fwd_timing": tf, "bwd_timing": tb,
            "fwd_roofline": roofline("mfma", ff, af, "fa::fwd_ring_kernel<128, 8, 2, 1, true>", flops_per_launch=ff),
            "bwd_roofline": roofline("mfma", fb, ab, " + ".join(BWD_KERNELS) + " (one fa_bwd call)",
-                                    "bwd_bf16_causal_d128_B2H16N4096" if not override else None, BWD_SOURCES,
+                                    "bwd_bf16_causal_d128_B2H16N4096" if not override
+                                    else f"bwd_bf16_causal_gqa_d{w.d}_B{w.B}Hq{w.Hq}Hkv{w.Hkv}N{w.Nq}", BWD_SOURCES,
                                     flops_per_launch=fb)}
     if not args.no_parity:
         # one whole group of query heads (batch 0, K/V head 0) against the fp64 oracle

@@ -53,10 +53,29 @@ struct Fp8Tile {
     static_assert(IPW >= 1 && BN * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
 };
 
-// byte offset of 16-byte chunk c of row r in a tile (XOR swizzle over the row's chunks)
+// XOR swizzle of the 16-byte chunks of row r in a tile.  A row holds D bytes,
+// so 256 / D rows share one 256-byte line of the 64 LDS banks.  Two read
+// forms must be conflict-free: 16 lanes reading one chunk of 16 consecutive
+// rows (the K fragments), and the transposing byte reads of the V^T gather,
+// where 16 lanes read one chunk of rows {R..R+3, R+8..R+11} and the other 16
+// lanes of the same pass the neighbouring chunk.  d = 128 (two rows a line):
+// rows of one parity take the swizzle (r >> 1) & 7 with bits 0 and 1
+// swapped, a bijection over 16 consecutive rows that also splits rows R + t
+// and R + 8 + t across chunk pairs.  d = 64 (four rows a line): (r >> 2) & 3.
+template <int D>
+__device__ __forceinline__ int fp8_swz(int r) {
+    if constexpr (D == 128) {
+        const int i = (r >> 1) & 7;
+        return ((i & 1) << 1) | ((i >> 1) & 1) | (i & 4);
+    } else {
+        return (r >> 2) & 3;
+    }
+}
+
+// byte offset of 16-byte chunk c of row r in a tile
 template <int D>
 __device__ __forceinline__ int off8(int r, int c) {
-    return r * D + ((c ^ (r & (D / 16 - 1))) << 4);
+    return r * D + ((c ^ fp8_swz<D>(r)) << 4);
 }
 
 __device__ __forceinline__ f32x16 mfma_f8(const v8i& a, const v8i& b, const f32x16& c) {
@@ -118,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
         for (int i = 0; i < T::IPW; ++i) {
             const int sl = (wave * T::IPW + i) * 64 + lane;
             const int row = sl / T::CPR, pos = sl % T::CPR;
-            const size_t g = (size_t)min(blk * T::BN + row, kv_end - 1) * D + ((pos ^ (row & (T::CPR - 1))) << 4);
+            const size_t g = (size_t)min(blk * T::BN + row, kv_end - 1) * D + ((pos ^ fp8_swz<D>(row)) << 4);
             const int lds_off = (wave * T::IPW + i) * 64 * 16;
             __builtin_amdgcn_global_load_lds(kbase + g, (__attribute__((address_space(3))) void*)(kt + lds_off), 16,
                                              0, 0);
