@@ -332,10 +332,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int total = g * nqblk;   // (head, query block) steps
     const int wave_q_begin = CAUSAL ? max(0, kw - off) : 0;
 
-    // step -> (query head, first query row)
+    // step -> (query head, first query row).  Each head's query blocks are
+    // taken last first, so the workgroups of one K/V head, which start
+    // together (heaviest key blocks first) and share an XCD, stream the same
+    // Q and dO tiles at the same time instead of each from its own causal
+    // start, and read them from that XCD's L2.
     auto step_rows = [&](int step, size_t& base, int& q0) {
         const int hq = hk * g + step / nqblk;
-        q0 = (qb0 + step % nqblk) * T::BQ;
+        q0 = (qb0 + nqblk - 1 - step % nqblk) * T::BQ;   // last query block first
         base = (size_t)(b * Hq + hq) * Nq;
     };
     // this wave's share of step `step` into ring slot `slot` (steps past the
