@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     extern __shared__ __align__(16) uint16_t smem[];
     const int id = blockIdx.x;
     const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-    const int bh = id % BH;
-    const int b = bh / Hq, h = bh % Hq;
+    int b, h;
+    group_major_head(id % BH, BH / Hq, Hq, Hkv, b, h);
     const int hk = h / (Hq / Hkv);
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, hf = lane >> 5;

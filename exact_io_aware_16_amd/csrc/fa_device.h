@@ -166,6 +166,19 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// (batch, query head) of launch position j in [0, B*Hq) of a kernel whose
+// workgroups run over (position, head) pairs: the query heads of one K/V
+// group sit B*Hkv positions apart, so with B*Hkv a multiple of 8 they land on
+// one XCD (workgroup w runs on XCD w mod 8, the dispatcher's round robin)
+// and read their shared K/V head through that XCD's L2.  With Hq == Hkv this
+// is b = j / Hq, h = j % Hq.
+__device__ __forceinline__ void group_major_head(int j, int B, int Hq, int Hkv, int& b, int& h) {
+    const int BK = B * Hkv, g = Hq / Hkv;
+    const int gi = j / BK, bk = j % BK;
+    b = bk / Hkv;
+    h = (bk % Hkv) * g + gi;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {

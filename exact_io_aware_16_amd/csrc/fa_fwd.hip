@@ -393,8 +393,8 @@ __global__ __launch_bounds__(NW * 64, ((NW == 4 && D * NT <= 128) ? kRingWgPerCu
     float sl2) {
     extern __shared__ __align__(16) uint16_t smem[];
     const int slot = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
-    const int b = bh / Hq, h = bh % Hq;
+    int b, h;
+    group_major_head(blockIdx.x % BH, BH / Hq, Hq, Hkv, b, h);
     fwd_qblock_ring<D, NW, S, NT, CAUSAL>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, b, h, CAUSAL ? nqb - 1 - slot : slot, sl2,
                                           smem);
 }

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(
     using T = Fp8Tile<D, NW, S>;
     extern __shared__ __align__(16) uint8_t smem8[];
     const int slot = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
-    const int b = bh / Hq, h = bh % Hq;
+    int b, h;
+    group_major_head(blockIdx.x % BH, BH / Hq, Hq, Hkv, b, h);
     const int qb = CAUSAL ? nqb - 1 - slot : slot;
     const int hk = h / (Hq / Hkv);
     const int tid = threadIdx.x;
